@@ -1,0 +1,228 @@
+"""The three decoding modes on the CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only tests, the package's ``smoke()`` check and the benchmark's CPU-baseline
+leg may use this module.
+
+``OracleSession`` mirrors the library's calls (prefill, diffuse_step,
+draft_block, verify_block, commit_kv, decode_ar) one for one, so a test can run
+the GPU and the oracle in lockstep.  The generation loops below it are the
+modes as the pages state them:
+
+* AR: one token per forward, left to right (ai-feeds "inference: three
+  modes", item 1; fintech-frontier-insights "three generation modes",
+  autoregressive bullet).
+* Block diffusion: a 32-token block is denoised in parallel over several
+  rounds (fintech-frontier-insights, diffusion bullet; ai-feeds item 2).  Each
+  round unmasks the masked positions whose confidence clears a threshold,
+  and always at least the most confident one; a step budget caps the rounds
+  (aimodeling English text: fewer refinement steps cut the inference budget).
+* Self-speculation: diffusion drafts a block in parallel and AR verifies it in
+  one forward (ai-feeds item 3; hotpaper abstract point (2)).  The draft is
+  kept up to the first token the AR argmax disagrees with; the AR token at
+  that point is emitted in its place (gsyq.cn explainer, section 2.3, the
+  classic verify rule).  At temperature 0 the output equals greedy AR
+  (fintech-frontier-insights, self-speculation bullet and accuracy list).
+
+Readings of open points (listed in the design notes): the row at a MASK
+position predicts that position in a bidirectional forward, while causal rows
+predict the next position; a self-spec draft is one bidirectional forward over
+[anchor, MASK x (B-1)]; confidence is the max softmax probability over the
+non-MASK vocabulary, compared with a strict ">"; confidence ties go to the
+lowest position; a finished diffusion block is committed through a causal
+forward, so the cache holds causal K/V in every mode.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from .model import BIDIR, CAUSAL, KVCache, OracleModel, select_rows
+
+
+@dataclass
+class RowSel:
+    tok: np.ndarray
+    conf: np.ndarray
+    margin: np.ndarray
+    logits: Optional[np.ndarray] = None
+
+
+def unmask_rule(block: np.ndarray, tok: np.ndarray, conf: np.ndarray, tau: float,
+                force_all: bool, mask_id: int):
+    """One denoising step's selection on one block.
+
+    Masked set Mk = positions still holding MASK.  U = {i in Mk: conf_i > tau}
+    plus the most confident i in Mk (lowest i on ties); on the last allowed
+    step U = Mk.  Returns (new block, U as a sorted index array, |Mk \\ U|).
+    """
+    block = np.array(block, dtype=np.int32, copy=True)
+    masked = np.nonzero(block == mask_id)[0]
+    if masked.size == 0:
+        return block, masked, 0
+    if force_all:
+        U = masked
+    else:
+        c = conf[masked]
+        best = masked[int(np.argmax(c))]            # argmax: first (lowest i) on ties
+        U = np.union1d(masked[c > tau], [best]).astype(np.int64)
+    block[U] = tok[U]
+    return block, U, int(masked.size - U.size)
+
+
+def accept_length(block: np.ndarray, ar_tok: np.ndarray) -> int:
+    """L = k + 1, k = largest k <= B-1 with block[j] == ar_tok[j-1] for all 1 <= j <= k."""
+    B = len(block)
+    k = 0
+    while k + 1 <= B - 1 and block[k + 1] == ar_tok[k]:
+        k += 1
+    return k + 1
+
+
+class OracleSession:
+    """Per-sequence caches plus the library's call surface."""
+
+    def __init__(self, model: OracleModel, keep_logits: bool = True):
+        self.model = model
+        self.mask_id = model.shape.mask_id
+        self.caches: Dict[int, KVCache] = {}
+        self.keep_logits = keep_logits
+        self.forwards = 0
+
+    def _cache(self, seq: int) -> KVCache:
+        if seq not in self.caches:
+            self.caches[seq] = self.model.new_cache()
+        return self.caches[seq]
+
+    def _sel(self, logits: np.ndarray) -> RowSel:
+        tok, conf, margin = select_rows(logits, self.mask_id)
+        return RowSel(tok, conf, margin, logits if self.keep_logits else None)
+
+    def committed(self, seq: int) -> int:
+        return self._cache(seq).n
+
+    # -- calls -------------------------------------------------------------
+    def prefill(self, seq: int, tokens: Sequence[int]) -> RowSel:
+        """Causal forward over the prompt; commits it; row P-1 gives y1."""
+        c = self._cache(seq)
+        assert c.n == 0
+        logits = self.model.forward(c, tokens, CAUSAL, logits_rows=[len(tokens) - 1])
+        c.n = len(tokens)
+        self.forwards += 1
+        return self._sel(logits)
+
+    def decode_ar(self, seq: int, token: int) -> RowSel:
+        """Causal forward over one token at position n; commits it."""
+        c = self._cache(seq)
+        logits = self.model.forward(c, [token], CAUSAL)
+        c.n += 1
+        self.forwards += 1
+        return self._sel(logits)
+
+    def draft_block(self, seq: int, anchor: int, B: int):
+        """Bidirectional forward over [anchor, MASK x (B-1)] -> (block, rows)."""
+        c = self._cache(seq)
+        blk = np.full(B, self.mask_id, dtype=np.int32)
+        blk[0] = anchor
+        sel = self._sel(self.model.forward(c, blk, BIDIR))
+        self.forwards += 1
+        blk[1:] = sel.tok[1:]
+        return blk, sel
+
+    def verify_block(self, seq: int, block: Sequence[int]):
+        """Causal forward over the block -> (AR argmax per row, L, rows)."""
+        c = self._cache(seq)
+        block = np.asarray(block, dtype=np.int32)
+        sel = self._sel(self.model.forward(c, block, CAUSAL))
+        self.forwards += 1
+        return sel.tok.copy(), accept_length(block, sel.tok), sel
+
+    def commit_kv(self, seq: int, n_accept: int):
+        self._cache(seq).n += int(n_accept)
+
+    def diffuse_step(self, seq: int, block: Sequence[int], tau: float, force_all: bool):
+        """Bidirectional forward over the block, then the unmask rule."""
+        c = self._cache(seq)
+        sel = self._sel(self.model.forward(c, block, BIDIR))
+        self.forwards += 1
+        new, U, n_left = unmask_rule(np.asarray(block), sel.tok, sel.conf, tau, force_all, self.mask_id)
+        return new, U, n_left, sel
+
+
+# -- generation loops -----------------------------------------------------------
+@dataclass
+class GenResult:
+    tokens: List[int]
+    forwards: int
+    accept_lengths: List[int] = field(default_factory=list)
+    steps_per_block: List[int] = field(default_factory=list)
+    margins: List[float] = field(default_factory=list)
+
+    @property
+    def tpf(self) -> float:
+        return len(self.tokens) / max(1, self.forwards)
+
+
+def generate_ar(model: OracleModel, prompt: Sequence[int], n_tokens: int, seq: int = 0) -> GenResult:
+    sess = OracleSession(model, keep_logits=False)
+    first = sess.prefill(seq, prompt)
+    toks, margins = [int(first.tok[0])], [float(first.margin[0])]
+    while len(toks) < n_tokens:
+        r = sess.decode_ar(seq, toks[-1])
+        toks.append(int(r.tok[0]))
+        margins.append(float(r.margin[0]))
+    return GenResult(toks, sess.forwards - 1, margins=margins)
+
+
+def generate_selfspec(model: OracleModel, prompt: Sequence[int], n_tokens: int, B: int,
+                      forced: Optional[Sequence[int]] = None, seq: int = 0) -> GenResult:
+    """Linear self-speculation.  ``forced`` replaces the natural accept length
+    cycle by cycle (a throughput schedule; the output is then not AR's)."""
+    sess = OracleSession(model, keep_logits=False)
+    first = sess.prefill(seq, prompt)
+    toks = [int(first.tok[0])]
+    Ls: List[int] = []
+    cyc = 0
+    while len(toks) < n_tokens:
+        blk, _ = sess.draft_block(seq, toks[-1], B)
+        a, L, _ = sess.verify_block(seq, blk)
+        if forced is not None:
+            L = int(forced[cyc])
+        sess.commit_kv(seq, L)
+        toks += [int(t) for t in blk[1:L]] + [int(a[L - 1])]
+        Ls.append(L)
+        cyc += 1
+    return GenResult(toks[:n_tokens], sess.forwards - 1, accept_lengths=Ls)
+
+
+def generate_diffusion(model: OracleModel, prompt: Sequence[int], n_tokens: int, B: int,
+                       tau: float, max_steps: Optional[int] = None, seq: int = 0) -> GenResult:
+    """Block diffusion: each block starts all-MASK; steps until none is left
+    (step ``max_steps``-1 unmasks everything); then a causal commit forward."""
+    sess = OracleSession(model, keep_logits=False)
+    sess.prefill(seq, prompt)
+    mask = model.shape.mask_id
+    toks: List[int] = []
+    steps: List[int] = []
+    while len(toks) < n_tokens:
+        blk = np.full(B, mask, dtype=np.int32)
+        s = 0
+        while True:
+            force = max_steps is not None and s == max_steps - 1
+            blk, _, left, _ = sess.diffuse_step(seq, blk, tau, force)
+            s += 1
+            if left == 0:
+                break
+        sess.verify_block(seq, blk)
+        sess.commit_kv(seq, B)
+        toks += [int(t) for t in blk]
+        steps.append(s)
+    return GenResult(toks[:n_tokens], sess.forwards - 1, steps_per_block=steps)
+
+
+def generate_diffusion_batch(model: OracleModel, prompts: Sequence[Sequence[int]], n_tokens: int,
+                             B: int, tau: float, max_steps: Optional[int] = None):
+    """Several sequences in lockstep per block.  In the oracle the sequences
+    never interact, so this is each sequence decoded on its own."""
+    return [generate_diffusion(model, p, n_tokens, B, tau, max_steps, seq=i) for i, p in enumerate(prompts)]
