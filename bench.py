@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark: decoded tokens/s of self-speculative block decoding on one GPU,
+8B-shaped random-init decoder (36 layers, d 4096, 32 q / 8 KV heads of 128,
+SwiGLU 12288, vocab 151936, bf16), single query, prompt 1024, block 32,
+2048 generated tokens, accept length per cycle drawn from a seeded uniform
+schedule over {1..32} (random weights accept ~1 token naturally, the schedule
+exercises long accepts).  A step is one self-speculation cycle: a
+bidirectional draft forward, a causal verify forward and the KV commit.
+
+Prints one JSON line (rank 0, N = 1).  Also reported: the roofline of the
+dominant kernel (the gate/up GEMM, measured with HIP events on the model's
+stream), per-kernel and per-forward latencies, AR and natural-accept
+self-speculation rates, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decoded tokens/s at 1 GPU, 8B-shape self-spec block 32; forward % of HBM roofline"
+
+
+def layer_weight_bytes(s) -> dict:
+    d, F = s.d_model, s.ffn_dim
+    return {"qkv": s.qkv_dim * d * 2, "o": d * s.q_dim * 2, "gate_up": 2 * F * d * 2, "down": d * F * 2}
+
+
+def forward_bytes(s, n: int, T: int) -> int:
+    """Algorithmic HBM bytes of one T-row forward at committed length n:
+    every weight once, the KV prefix read, the block's K/V written, the
+    gathered embedding rows."""
+    w = sum(layer_weight_bytes(s).values()) * s.n_layers + s.vocab * s.d_model * 2
+    kv_tok = s.n_layers * 2 * s.n_kv_heads * s.head_dim * 2
+    return w + (n + T) * kv_tok + T * kv_tok + T * s.d_model * 2
+
+
+def kernel_bytes(s, cls: str, M: int) -> int:
+    """Algorithmic bytes of one launch of a GEMM class at M rows: weights +
+    activations in + activations out."""
+    d, F = s.d_model, s.ffn_dim
+    lw = layer_weight_bytes(s)
+    io = {"qkv": M * d * 2 + M * s.qkv_dim * 2, "o": M * s.q_dim * 2 + 2 * M * d * 4,
+          "gate_up": M * d * 2 + M * F * 2, "down": M * F * 2 + 2 * M * d * 4}
+    return lw[cls] + io[cls]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed self-spec cycles (default: 2048 tokens)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--gen-tokens", type=int, default=2048)
+    ap.add_argument("--prompt", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline pass only (for profilers)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not part of it "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from self_speculative_amd.decode import SelfSpecRun, prefill
+    from self_speculative_amd.model import Model
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+    s = W.SHAPES["8b"]
+    B = 32
+    t0 = time.time()
+    weights = W.make_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
+    log(f"weights drawn in {time.time() - t0:.1f}s")
+    prompt = W.prompt_ids(s, args.prompt, seed=0)
+    sched = W.forced_accept_schedule(8192, B, seed=0)
+    K = args.steps
+    if K is None:
+        tot, K = 1, 0
+        while tot < args.gen_tokens:
+            tot += int(sched[K])
+            K += 1
+    max_ctx = 4096 if args.prompt + args.gen_tokens + 2 * B <= 4096 else args.prompt + args.gen_tokens + 1024
+    t0 = time.time()
+    model = Model(s, weights, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=128)
+    torch.cuda.synchronize()
+    log(f"model uploaded + packed in {time.time() - t0:.1f}s ({model.weight_bytes / 1e9:.2f} GB)")
+    dev = model.device
+
+    def run_cycles(seq, n_cyc, sched_vals, first):
+        run = SelfSpecRun(model, B, seq)
+        blocks = torch.empty((n_cyc, B), dtype=torch.int32, device=dev)
+        ars = torch.empty((n_cyc, B), dtype=torch.int32, device=dev)
+        anchor = first.data_ptr()
+        Ls = []
+        for c in range(n_cyc):
+            run.block, run.ar = blocks[c], ars[c]
+            L = run.cycle(anchor, None if sched_vals is None else int(sched_vals[c]))
+            Ls.append(L)
+            anchor = ars[c].data_ptr() + 4 * (L - 1)
+        return Ls, anchor
+
+    # warm-up on sequence 1
+    first = prefill(model, 1, prompt)
+    run_cycles(1, args.warmup, W.forced_accept_schedule(args.warmup, B, seed=1), first)
+    torch.cuda.synchronize()
+    model.seq_reset(1)
+
+    # headline: K forced cycles on sequence 0
+    first = prefill(model, 0, prompt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    Ls, _ = run_cycles(0, K, sched[:K], first)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    tokens = int(sum(Ls))
+    value = tokens / wall
+    log(f"self-spec forced: {K} cycles, {tokens} tokens in {wall * 1e3:.1f} ms -> {value:.1f} tok/s")
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (random-init N(0,0.02^2) bf16 weights, uniform random prompt ids, seed 0)",
+           "config": {"workload": "8B-shape decoder (36 layers, d 4096, 32/8 heads x 128, FFN 12288, vocab 151936), "
+                                  "single query, prompt 1024, self-speculation block 32, forced accept L~U{1..32} "
+                                  "seed 0, 2048 generated tokens",
+                      "prompt_len": args.prompt, "generated_tokens": tokens + 1, "block": B,
+                      "accept_schedule": "forced uniform {1..32}, seed 0"}}
+
+    if not args.no_extras:
+        # per-kernel-class timing passes (HIP events on the model's stream)
+        ctx_n = args.prompt
+        model.seq_reset(1)
+        first = prefill(model, 1, prompt)
+        anchor_t = first
+        per = {}
+        n_cyc = 6
+        classes = ["gate_up", "down", "qkv", "o", "attn", "attn_combine", "norm", "lm_head", "finish", "forward"]
+        extra_sched = W.forced_accept_schedule(n_cyc * len(classes), B, seed=2)
+        pos = 0
+        anchor_addr = first.data_ptr()
+        run = SelfSpecRun(model, B, 1)
+        ring_b = torch.empty((n_cyc * len(classes), B), dtype=torch.int32, device=dev)
+        ring_a = torch.empty((n_cyc * len(classes), B), dtype=torch.int32, device=dev)
+        fwd_ns = []
+        for cls in classes:
+            torch.cuda.synchronize()
+            model.timing_start(cls, 4096)
+            for c in range(n_cyc):
+                run.block, run.ar = ring_b[pos], ring_a[pos]
+                fwd_ns.append(model.seq_length(1))
+                L = run.cycle(anchor_addr, int(extra_sched[pos]))
+                anchor_addr = ring_a[pos].data_ptr() + 4 * (L - 1)
+                pos += 1
+            n, tot_ms, mn, mx = model.timing_stop()
+            per[cls] = {"launches": n, "avg_us": round(tot_ms / max(1, n) * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                        "max_us": round(mx * 1e3, 2)}
+            log(f"{cls:>12}: {n} launches, avg {per[cls]['avg_us']} us")
+        # roofline of the dominant kernel (gate/up GEMM: 47% of a forward's bytes)
+        gu = per["gate_up"]
+        gu_bytes = kernel_bytes(s, "gate_up", B)
+        achieved = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": "k_gemm_bf16<EPI_SWIGLU> (gate/up + SwiGLU), M=32",
+                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "bytes_per_launch": gu_bytes, "avg_launch_us": gu["avg_us"]}
+        # whole forward vs roofline
+        f_us = per["forward"]["avg_us"]
+        mean_n = statistics.mean(fwd_ns[-n_cyc:])
+        fb = forward_bytes(s, int(mean_n), B)
+        out["forward"] = {"avg_us": f_us, "algorithmic_bytes": fb, "hbm_frac": round(fb / (f_us * 1e-6) / 8e12, 4),
+                          "mean_committed_len": round(mean_n, 1)}
+        kern = {}
+        for cls in ("qkv", "o", "gate_up", "down"):
+            b = kernel_bytes(s, cls, B)
+            kern[cls] = dict(per[cls], GBps=round(b / (per[cls]["avg_us"] * 1e-6) / 1e9, 1))
+        for cls in ("attn", "attn_combine", "norm", "lm_head", "finish"):
+            kern[cls] = per[cls]
+        kern["lm_head"]["GBps"] = round(s.vocab * s.d_model * 2 / (per["lm_head"]["avg_us"] * 1e-6) / 1e9, 1)
+        out["kernels"] = kern
+        # natural-accept self-spec and AR rates (short windows)
+        model.seq_reset(1)
+        first = prefill(model, 1, prompt)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        Ln, _ = run_cycles(1, 16, None, first)
+        torch.cuda.synchronize()
+        t_nat = time.perf_counter() - t0
+        model.seq_reset(1)
+        first = prefill(model, 1, prompt)
+        ar_out = torch.empty(65, dtype=torch.int32, device=dev)
+        ar_out[0:1].copy_(first)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        base = ar_out.data_ptr()
+        for t in range(1, 65):
+            model.decode_ar(1, base + 4 * (t - 1), base + 4 * t)
+        torch.cuda.synchronize()
+        t_ar = time.perf_counter() - t0
+        # prefill latency
+        model.seq_reset(1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        prefill(model, 1, prompt)
+        torch.cuda.synchronize()
+        t_pf = time.perf_counter() - t0
+        out["modes"] = {"selfspec_natural": {"cycles": 16, "tokens": int(sum(Ln)), "tok_per_s": round(sum(Ln) / t_nat, 1),
+                                             "mean_accept": round(float(np.mean(Ln)), 3)},
+                        "ar": {"tokens": 64, "tok_per_s": round(64 / t_ar, 1), "ms_per_token": round(t_ar / 64 * 1e3, 3)},
+                        "selfspec_forced": {"tok_per_s": round(value, 1), "mean_accept": round(tokens / K, 3),
+                                            "tpf": round(tokens / (2 * K), 3)},
+                        "prefill_1024_ms": round(t_pf * 1e3, 2)}
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(s, weights, prompt, tokens / K, log)
+    model.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(s, weights, prompt, tokens_per_cycle, log) -> dict:
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    prefill of the first 32 prompt tokens (setup, untimed), then one
+    self-speculation cycle (bidirectional draft + causal verify of 32 rows)
+    timed; the rate is the headline's tokens per cycle over that cycle time."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except Exception:  # pragma: no cover
+        blas_threads = 0
+    cores = len(os.sched_getaffinity(0))
+    om = O.OracleModel(s, weights)
+    sess = O.OracleSession(om, keep_logits=False)
+    t0 = time.time()
+    first = sess.prefill(0, prompt[:32])
+    log(f"oracle setup (prefill 32, weight widening) {time.time() - t0:.1f}s")
+    t0 = time.perf_counter()
+    blk, _ = sess.draft_block(0, int(first.tok[0]), 32)
+    sess.verify_block(0, blk)
+    dt = time.perf_counter() - t0
+    log(f"oracle cycle {dt:.1f}s")
+    return {"value": round(tokens_per_cycle / dt, 4), "unit": "tokens/s", "cores": int(blas_threads or cores),
+            "kind": "oracle",
+            "sample": f"one self-spec cycle (32-row bidirectional draft + 32-row causal verify, float64 NumPy, "
+                      f"36 layers) at committed length 32, {dt:.1f}s; rate = {tokens_per_cycle:.2f} tokens per "
+                      f"cycle (the headline schedule's mean) / cycle time; host has {cores} cores"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,211 @@
+/*
+ * sdm.h -- C ABI of the block-wise decoding forward (AR / block diffusion /
+ * self-speculation) for one AMD Instinct MI355X (gfx950).
+ *
+ * The method: one decoder serves three decoding modes, which differ only in
+ * the attention mask of the block and in how tokens are chosen from the
+ * logits (Nemotron-Labs-Diffusion pages: ai-feeds "inference: three modes";
+ * fintech-frontier-insights "three generation modes"; hotpaper abstract).
+ *   - AR: one token per forward (sdm_decode_ar).
+ *   - Block diffusion: a block of MASK placeholders is denoised in parallel
+ *     over several forwards; each step unmasks the masked positions whose
+ *     confidence clears a threshold (sdm_diffuse_step), then the finished
+ *     block is committed through a causal forward (sdm_verify_block +
+ *     sdm_commit_kv).
+ *   - Self-speculation: a bidirectional forward drafts a block
+ *     (sdm_draft_block), one causal forward verifies it (sdm_verify_block),
+ *     and the longest prefix matching the AR argmax plus one AR token is kept
+ *     (sdm_commit_kv).  At temperature 0 the output equals greedy AR
+ *     (fintech-frontier-insights, self-speculation bullet).
+ *
+ * Conventions for every call
+ *   - d_ pointers are device pointers, h_ pointers host pointers.  The caller
+ *     owns every buffer (weights, KV pool, workspace, inputs, outputs) and
+ *     keeps them alive until sdm_free_model.  The library owns only the
+ *     model handle and host-side bookkeeping.
+ *   - Calls are asynchronous on the HIP stream given to sdm_init_model;
+ *     outputs are valid once that stream has been synchronised.
+ *   - Every call validates its arguments and the sequence state before it
+ *     enqueues anything: a call that returns an error has changed nothing.
+ *     The message of the last error on the calling thread is returned by
+ *     sdm_last_error().
+ *   - A handle must not be used from two threads at once.
+ *
+ * Numerics.  bf16 models keep weights, normalised activations, q/k/v after
+ * RoPE (hence the KV cache), the attention output and the SwiGLU product in
+ * bf16 (round to nearest, ties to even); every contraction accumulates in
+ * fp32; the residual stream and logits are fp32.  f32 models keep all of it
+ * in fp32.  The MASK id never wins an argmax and is left out of the softmax.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sdm_model sdm_model; /* opaque, library-owned host object */
+
+typedef enum {
+  SDM_OK = 0,
+  SDM_ERR_ARG = -1,        /* null pointer, size or id out of range          */
+  SDM_ERR_STATE = -2,      /* call not allowed in the sequence's state        */
+  SDM_ERR_CAPACITY = -3,   /* KV pool / context / workspace / seq slots full  */
+  SDM_ERR_DEVICE = -4,     /* a HIP call failed; sticky for the handle        */
+  SDM_ERR_UNSUPPORTED = -5 /* shape or dtype this build does not implement    */
+} sdm_status;
+
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+typedef enum { SDM_CAUSAL = 0, SDM_BIDIR = 1 } sdm_attn_mode;
+
+/* Model and capacity description.
+ *   dtype bf16 requires head_dim 128, d_model and q/kv widths multiples of 32,
+ *   ffn_dim a multiple of 16 and vocab a multiple of 32; f32 requires an even
+ *   head_dim.  n_q_heads must be a multiple of n_kv_heads.  mask_id is the
+ *   reserved MASK token (vocab - 1 in every shipped shape).  page_tokens must
+ *   be 64.  max_rows bounds the rows of one forward (n_seq * block, or a
+ *   prefill chunk); max_context bounds a sequence's length (prompt + output
+ *   + one block). */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, mask_id;
+  float rope_base, rms_eps;
+  int32_t dtype;
+  int32_t page_tokens, max_seqs, max_block, max_context, max_rows;
+} sdm_config;
+
+/* Device weights in the library's layout (see sdm_pack_matrix).  Gains are
+ * [d_model] vectors in the model dtype; matrices are packed.  The per-layer
+ * members are host arrays of n_layers device pointers; the arrays are copied
+ * by sdm_init_model.
+ *   embed     [vocab, d_model] row-major, NOT packed (rows are gathered)
+ *   lm_head   packed SDM_PACK_PLAIN of [vocab, d_model]
+ *   w_qkv     packed SDM_PACK_QKV of [(Hq + 2 Hkv) * hd, d_model] (q rows, k rows, v rows)
+ *   w_o       packed SDM_PACK_PLAIN of [d_model, Hq * hd]
+ *   w_gate_up packed SDM_PACK_GATE_UP of gate [ffn, d_model] and up [ffn, d_model]
+ *   w_down    packed SDM_PACK_PLAIN of [d_model, ffn]                                 */
+typedef struct {
+  const void *embed, *final_norm, *lm_head;
+  const void *const *attn_norm, *const *w_qkv, *const *w_o;
+  const void *const *ffn_norm, *const *w_gate_up, *const *w_down;
+} sdm_weights;
+
+typedef enum { SDM_PACK_PLAIN = 0, SDM_PACK_QKV = 1, SDM_PACK_GATE_UP = 2 } sdm_pack_kind;
+
+/* Bytes of device workspace a model with this config needs (0 on a bad config). */
+size_t sdm_workspace_bytes(const sdm_config* cfg);
+/* Bytes of one KV page (all layers' K and V of page_tokens positions). */
+size_t sdm_kv_page_bytes(const sdm_config* cfg);
+/* Bytes of a packed [rows, cols] matrix of the config's dtype. */
+size_t sdm_packed_bytes(const sdm_config* cfg, int64_t rows, int64_t cols);
+
+/* Rearrange a row-major [rows, cols] matrix (out-major: row = output feature)
+ * into the layout the GEMM kernels stream.  For SDM_PACK_GATE_UP, d_src is the
+ * gate matrix and d_src2 the up matrix, each [rows, cols], and the result holds
+ * 2*rows rows.  A pure permutation: no arithmetic.  Enqueued on hip_stream. */
+sdm_status sdm_pack_matrix(const sdm_config* cfg, int32_t kind, const void* d_src, const void* d_src2,
+                           void* d_dst, int64_t rows, int64_t cols, void* hip_stream);
+
+/* Create a model.  kv_pool holds n_pages pages of sdm_kv_page_bytes; the
+ * workspace holds ws_bytes >= sdm_workspace_bytes.  Uploads the RoPE table
+ * (angles p * base^(-2t/hd) in fp64, cos/sin stored fp32) into the workspace. */
+sdm_status sdm_init_model(const sdm_config* cfg, const sdm_weights* w, void* kv_pool, int64_t n_pages,
+                          void* workspace, size_t ws_bytes, void* hip_stream, sdm_model** out);
+
+/* Causal forward over the prompt d_tokens[n] of an empty sequence, in chunks of
+ * at most max_rows rows; commits all n positions.  d_next_token[0] = argmax of
+ * the last row (the first generated token).  d_logits (nullable) receives the
+ * last row's logits [vocab] fp32. */
+sdm_status sdm_prefill(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t* d_next_token,
+                       float* d_logits);
+
+/* One denoising step for n_seq sequences in lockstep (ids in h_seq_ids).
+ * d_block [n_seq][B] holds each sequence's block (MASK where still masked) and
+ * is updated in place.  A bidirectional forward over the blocks at positions
+ * n..n+B-1; the row at a masked position predicts that position.  Per
+ * sequence, over its masked set Mk: U = {i in Mk : conf_i > tau} plus the most
+ * confident i in Mk (lowest i on ties); force_all != 0 makes U = Mk.  Positions
+ * in U take their argmax token; d_n_masked[s] = |Mk \ U|.  conf is the max
+ * softmax probability over non-MASK ids.  d_conf (nullable) [n_seq][B] gets
+ * every row's conf; d_logits (nullable) [n_seq*B][vocab].  K/V of the block
+ * are written to the uncommitted slots and are not committed. */
+sdm_status sdm_diffuse_step(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, int32_t* d_block, int32_t B,
+                            float tau, int32_t force_all, int32_t* d_n_masked, float* d_conf, float* d_logits);
+
+/* Self-spec draft: a bidirectional forward over [anchor, MASK x (B-1)] at
+ * positions n..n+B-1.  d_block_out[B] = anchor then the argmax of rows 1..B-1. */
+sdm_status sdm_draft_block(sdm_model* m, int32_t seq, const int32_t* d_anchor, int32_t B, int32_t* d_block_out,
+                           float* d_logits);
+
+/* Causal forward over d_block [n_seq][B] (position j at n+j) for each sequence.
+ * d_ar_argmax [n_seq][B]: row j's argmax (the AR prediction of position n+j+1).
+ * d_accept_len [n_seq]: L = k+1, k the largest k <= B-1 with block[j] ==
+ * argmax[j-1] for all 1 <= j <= k (the classic verify rule, gsyq.cn explainer
+ * section 2.3).  The block's causal K/V become committable (sdm_commit_kv). */
+sdm_status sdm_verify_block(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, const int32_t* d_block, int32_t B,
+                            int32_t* d_ar_argmax, int32_t* d_accept_len, float* d_logits);
+
+/* Commit the first n_accept (1..B of the last verify) positions of the last
+ * causal block forward of seq.  Requires a preceding sdm_verify_block on seq. */
+sdm_status sdm_commit_kv(sdm_model* m, int32_t seq, int32_t n_accept);
+
+/* AR: causal forward over d_token[0] at position n, commit it, d_next_token[0]
+ * = argmax. */
+sdm_status sdm_decode_ar(sdm_model* m, int32_t seq, const int32_t* d_token, int32_t* d_next_token, float* d_logits);
+
+/* Per-row selection of the last forward: token, conf and top-2 margin, each
+ * [rows] (nullable).  Device-to-device copies on the model's stream. */
+sdm_status sdm_row_stats(sdm_model* m, int32_t* d_tok, float* d_conf, float* d_margin);
+
+/* Release a sequence's pages and reset it to empty. */
+sdm_status sdm_seq_reset(sdm_model* m, int32_t seq);
+/* Committed length of a sequence (host-side value). */
+sdm_status sdm_seq_length(const sdm_model* m, int32_t seq, int32_t* out);
+/* Number of free KV pages. */
+int64_t sdm_free_pages(const sdm_model* m);
+/* Reorder the free-page list with a seeded shuffle (layout independence tests). */
+sdm_status sdm_shuffle_free_pages(sdm_model* m, uint64_t seed);
+
+sdm_status sdm_free_model(sdm_model* m);
+const char* sdm_last_error(void);
+
+/* ---- kernel timing (measurement) -------------------------------------------
+ * While a timing window is open, the runtime records a hipEvent pair on the
+ * model's stream around every launch of one kernel class (or around whole
+ * forwards), up to `capacity` launches.  sdm_timing_stop synchronises the
+ * stream, returns the number of timed launches and their summed / shortest /
+ * longest duration in milliseconds, and closes the window. */
+typedef enum {
+  SDM_K_QKV = 0, SDM_K_ATTN = 1, SDM_K_ATTN_COMBINE = 2, SDM_K_O = 3, SDM_K_GATE_UP = 4, SDM_K_DOWN = 5,
+  SDM_K_LM_HEAD = 6, SDM_K_NORM = 7, SDM_K_FINISH = 8, SDM_K_FORWARD = 9
+} sdm_kernel_class;
+sdm_status sdm_timing_start(sdm_model* m, int32_t kernel_class, int32_t capacity);
+sdm_status sdm_timing_stop(sdm_model* m, int64_t* launches, double* total_ms, double* min_ms, double* max_ms);
+
+/* ---- standalone block attention (the op the decoder's layers run) --------
+ * q:  d_q [T, Hq, hd] bf16 row-major (already rotated).
+ * kv: d_k, d_v [n_prefix + T, Hkv, hd] bf16 row-major are first scattered into
+ *     pages of d_pool (sdm_attn_pack_kv) through the page table d_pages.
+ * out: d_out [T, Hq, hd] bf16, softmax(q.k / sqrt(hd)) over the visible keys
+ *     applied to v; key j visible to block row i iff j < n_prefix or
+ *     (j < n_prefix + T and (mode == SDM_BIDIR or j <= n_prefix + i)).
+ * hd must be 128, Hq a multiple of Hkv, 1 <= T <= 4096.  Every slot of the
+ * pages that hold keys [0, n_prefix + T) must contain finite values (zero the
+ * pool once): keys past the end of the last 32-key tile are read and given
+ * probability 0. */
+size_t sdm_attn_pool_bytes(int32_t n_kv_heads, int32_t head_dim, int32_t n_pages);
+size_t sdm_attn_workspace_bytes(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t T,
+                                int32_t max_keys);
+sdm_status sdm_attn_pack_kv(int32_t n_kv_heads, int32_t head_dim, const void* d_k, const void* d_v, int32_t n_keys,
+                            const int32_t* d_pages, void* d_pool, void* hip_stream);
+sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const void* d_q,
+                         const void* d_pool, const int32_t* d_pages, int32_t n_prefix, int32_t T, int32_t mode,
+                         void* d_out, void* d_workspace, size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDM_H */

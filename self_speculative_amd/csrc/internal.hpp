@@ -1,0 +1,146 @@
+// Internal declarations shared by the host runtime (sdm_runtime.cpp) and the
+// gfx950 kernels (sdm_kernels.hip).  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sdm {
+
+constexpr int kPageTokens = 64;        // KV page size (positions per page)
+constexpr int kAttnSplitKeys = 256;    // keys per attention split (absolute ranges)
+constexpr int kMaxSlots = 64;          // sequences in one forward
+constexpr int kHd = 128;               // bf16 path head dim
+
+enum Mode { CAUSAL = 0, BIDIR = 1 };
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3 };
+enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1 };
+
+// Element (r, c) of a [R, C] matrix in the MFMA 32x32x16 operand layout:
+// tiles of 32 rows x 16 columns, 1 KiB each, laid out row-tile major; inside
+// a tile lane = (r % 32) + 32 * ((c % 16) / 8) holds the 8 columns c%8.
+// The same layout serves the A operand (weights, rows = outputs) and the B
+// operand (activations, rows = tokens).
+__host__ __device__ inline int64_t packed_index(int64_t r, int64_t c, int64_t C) {
+  const int64_t rt = r >> 5, cb = c >> 4;
+  const int64_t lane = (r & 31) + 32 * ((c & 15) >> 3);
+  return (((rt * (C >> 4) + cb) * 64 + lane) << 3) + (c & 7);
+}
+
+// KV page (bf16 path), per layer and KV head: a K block then (after all
+// heads' K blocks) a V block, each kPageTokens x 128 elements.
+//   K block: A-operand tiles of 32 keys x 16 dims: [key/32][dim/16][64][8].
+//   V block: A-operand tiles of V^T, 32 dims x 16 keys: [dim/32][key/16][64][8],
+//            where inside a 16-key group the key held by (lane half h', e) is
+//            8*(e/4) + 4*h' + e%4 -- the order in which the attention kernel's
+//            score tile hands probabilities to the P.V product.
+__host__ __device__ inline int kv_k_index(int pk, int d) {
+  const int lane = (pk & 31) + 32 * ((d & 15) >> 3);
+  return ((((pk >> 5) * (kHd / 16) + (d >> 4)) * 64 + lane) << 3) + (d & 7);
+}
+__host__ __device__ inline int kv_v_index(int pk, int d) {
+  const int r = pk & 15;
+  const int hh = (r >> 2) & 1;
+  const int e = 4 * (r >> 3) + (r & 3);
+  const int lane = (d & 31) + 32 * hh;
+  return ((((d >> 5) * (kPageTokens / 16) + (pk >> 4)) * 64 + lane) << 3) + e;
+}
+
+struct Slots {
+  int n_seq;   // sequences in this forward
+  int T;       // rows per sequence
+  int ids[kMaxSlots];
+};
+
+struct KvView {
+  void* pool;            // page base
+  int64_t page_elems;    // elements per page
+  int64_t layer_off;     // element offset of this layer inside a page
+  const int* page_table; // [max_seqs][max_pages]
+  int max_pages;
+  const int* seq_len;    // committed length per sequence (block base n)
+  int Hkv, hd;
+};
+
+struct EpiArgs {
+  int M;                 // valid rows
+  Slots slots;
+  KvView kv;
+  int Hq;
+  uint16_t* q_out;       // QKV: [M][Hq][hd]
+  const float* rope_cos; // [max_context][hd/2]
+  const float* rope_sin;
+  float* x;              // RESID: residual [M][d]
+  int d;
+  uint16_t* h_out;       // SWIGLU: packed-B [M32][F]
+  int F;
+  float4* records;       // LOGITS: [M][n_vtiles] (max, idx bits, max2, sum)
+  int n_vtiles;
+  float* logits;         // LOGITS: optional [M][V]
+  int V, mask_id;
+};
+
+struct GemmShape {
+  int NT, KB;            // 32-row tiles of W, 16-column blocks of K
+  int MTILES;            // 32-row tiles of the activations
+};
+
+struct AttnArgs {
+  const uint16_t* q;     // [rows][Hq][hd] (row-major)
+  KvView kv;
+  Slots slots;
+  int Hq, mode;
+  float scale;
+  float* opart;          // [slots][Hkv][max_splits][nq_pad][hd]
+  float* mlpart;         // [slots][Hkv][max_splits][nq_pad][2]
+  int max_splits, nq_pad;
+  uint16_t* out;         // [rows][Hq*hd]: packed-B when out_packed else row-major
+  int out_packed;
+};
+
+struct FinishArgs {
+  int mode;              // Finish
+  Slots slots;
+  int M, T;              // rows, rows per slot
+  const float4* records; int n_vtiles;
+  int* tok; float* conf; float* margin;   // per-row results (workspace)
+  int mask_id;
+  const int* anchor;     // DRAFT: device anchor
+  int* block;            // DRAFT out / DIFFUSE in-out / VERIFY in [slots][T]
+  int* ar_out;           // VERIFY: [slots][T]
+  int* accept;           // VERIFY: [slots]
+  int* n_masked;         // DIFFUSE: [slots]
+  float* conf_out;       // DIFFUSE: optional [slots][T]
+  float tau; int force_all;
+  int* next;             // NEXT: device token (last row of slot 0)
+};
+
+// ---- launchers (sdm_kernels.hip) -------------------------------------------
+hipError_t launch_pack(int dtype, int kind, const void* src, const void* src2, void* dst, int64_t rows, int64_t cols,
+                       int head_dim, hipStream_t st);
+hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* tokens, int tok_src, const int* anchor,
+                        int M, int T, int mask_id, float* x, hipStream_t st);
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, float eps, int M, int d, int row0,
+                          void* out, hipStream_t st);
+hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
+                            hipStream_t st);
+hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st);
+hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_finish(const FinishArgs& f, hipStream_t st);
+
+// fp32 (VALU) path
+hipError_t launch_gemm_f32(const float* X, const float* W, int M, int N, int K, float* Y, hipStream_t st);
+hipError_t launch_qkv_post_f32(const float* Y, const EpiArgs& ea, int hd, hipStream_t st);
+hipError_t launch_attention_f32(const float* q, const KvView& kv, const Slots& sl, int Hq, int mode, float* out,
+                                hipStream_t st);
+hipError_t launch_resid_f32(const float* Y, float* x, int M, int d, hipStream_t st);
+hipError_t launch_swiglu_f32(const float* Y, float* h, int M, int F, hipStream_t st);
+hipError_t launch_logit_records_f32(const float* Y, const EpiArgs& ea, hipStream_t st);
+
+// bookkeeping
+hipError_t launch_set_ints(int* dst, const int* vals, int n, hipStream_t st);   // n <= 64, values by value
+hipError_t launch_attn_pack_kv(int Hkv, const uint16_t* k, const uint16_t* v, int n_keys, const int* pages,
+                               uint16_t* pool, hipStream_t st);
+
+}  // namespace sdm

@@ -1,0 +1,871 @@
+// gfx950 kernels of the block-wise decoding forward.
+//
+// bf16 path (the 3B/8B/14B-shaped decoders): skinny MFMA GEMMs that stream
+// packed weights once per forward with fused epilogues (RoPE + paged KV write,
+// residual add, SwiGLU, vocab partial reduction), MFMA block attention over the
+// paged KV cache with a split-KV combine, RMSNorm and the per-row selection
+// that implements the three modes' token rules.
+// f32 path (the tiny decoder): plain VALU kernels with the same semantics.
+//
+// The operations follow the decoder of the Nemotron-Labs-Diffusion pages as
+// restated in the public header: the attention pattern (prefix visible to the
+// whole block, block rows bidirectional when drafting/denoising and causal
+// when verifying; fintech-frontier-insights, training route / Efficient-DLM
+// block-wise attention), the threshold unmask of block diffusion
+// (fintech-frontier-insights, diffusion bullet) and the accept rule of
+// self-speculation (gsyq.cn explainer, section 2.3).
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+
+#include "internal.hpp"
+
+namespace sdm {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest, ties to even (finite inputs)
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Row of accumulator register r held by a lane of half h in a 32x32 MFMA C tile.
+__device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// Packing (one-time, a permutation)
+// ---------------------------------------------------------------------------
+// Row of the packed matrix that holds source row r.
+__device__ __forceinline__ int64_t pack_row(int kind, int64_t r, int64_t rows, int which, int head_dim) {
+  if (kind == 1) {  // QKV: per head, tiles of [16 dims of the first half, 16 partner dims]
+    const int64_t head = r / head_dim, dl = r % head_dim, half = dl / (head_dim / 2), t = dl % (head_dim / 2);
+    return head * head_dim + 32 * (t / 16) + 16 * half + (t % 16);
+  }
+  if (kind == 2) {  // GATE_UP: tiles of [16 gate features, the same 16 up features]
+    return 32 * (r / 16) + 16 * which + (r % 16);
+  }
+  return r;
+}
+
+__global__ void k_pack_bf16(int kind, const uint16_t* __restrict__ src, int which, uint16_t* __restrict__ dst,
+                            int64_t rows, int64_t cols, int64_t out_cols, int head_dim) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * cols) return;
+  const int64_t r = i / cols, c = i % cols;
+  dst[packed_index(pack_row(kind, r, rows, which, head_dim), c, out_cols)] = src[i];
+}
+
+__global__ void k_copy_f32(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+hipError_t launch_pack(int dtype, int kind, const void* src, const void* src2, void* dst, int64_t rows, int64_t cols,
+                       int head_dim, hipStream_t st) {
+  const int64_t n = rows * cols;
+  const dim3 blk(256), grd((unsigned)((n + 255) / 256));
+  if (dtype == 1) {
+    hipLaunchKernelGGL(k_pack_bf16, grd, blk, 0, st, kind, (const uint16_t*)src, 0, (uint16_t*)dst, rows, cols, cols,
+                       head_dim);
+    if (kind == 2)
+      hipLaunchKernelGGL(k_pack_bf16, grd, blk, 0, st, kind, (const uint16_t*)src2, 1, (uint16_t*)dst, rows, cols,
+                         cols, head_dim);
+  } else {
+    hipLaunchKernelGGL(k_copy_f32, grd, blk, 0, st, (const float*)src, (float*)dst, n);
+    if (kind == 2) hipLaunchKernelGGL(k_copy_f32, grd, blk, 0, st, (const float*)src2, (float*)dst + n, n);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block assembly + embedding gather into the fp32 residual stream
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+
+template <typename T>
+__global__ void k_embed(const T* __restrict__ E, int d, int V, const int* __restrict__ tokens, int tok_src,
+                        const int* __restrict__ anchor, int T_, int mask_id, float* __restrict__ x) {
+  const int m = blockIdx.x;
+  int tok;
+  if (tok_src == TOK_DRAFT) tok = (m % T_ == 0) ? anchor[m / T_] : mask_id;
+  else tok = tokens[m];
+  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // out-of-range ids are clamped, never read out of bounds
+  for (int k = threadIdx.x; k < d; k += blockDim.x) x[(int64_t)m * d + k] = load_as_f32<T>(E, (int64_t)tok * d + k);
+}
+
+hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* tokens, int tok_src, const int* anchor,
+                        int M, int T, int mask_id, float* x, hipStream_t st) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(256), 0, st, (const uint16_t*)E, d, V, tokens, tok_src,
+                       anchor, T, mask_id, x);
+  else
+    hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(256), 0, st, (const float*)E, d, V, tokens, tok_src, anchor, T,
+                       mask_id, x);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: y = (x / sqrt(mean(x^2) + eps)) * g.  One workgroup per row, fixed
+// reduction order.  bf16: rounded to bf16 straight into the packed B-operand
+// layout, 8 features (one 16-byte store) per thread and chunk.  f32: row-major.
+// ---------------------------------------------------------------------------
+constexpr int kNormChunks = 4;  // chunks of 8 features per thread: d <= 8192
+
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* __restrict__ x, const uint16_t* __restrict__ gain,
+                                                      float eps, int d, int row0, uint16_t* __restrict__ out) {
+  const int m = blockIdx.x;
+  const float* xr = x + (int64_t)(row0 + m) * d;
+  const int nch = d >> 3;
+  float v[kNormChunks][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kNormChunks; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nch) {
+      const float4 a = ((const float4*)xr)[2 * c], b = ((const float4*)xr)[2 * c + 1];
+      v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+      v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float r = sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < kNormChunks; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nch) {
+      const u32x4 gv = ((const u32x4*)gain)[c];
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g0 = __uint_as_float(gv[e] << 16), g1 = __uint_as_float(gv[e] & 0xffff0000u);
+        const uint16_t lo = f2bf((v[j][2 * e] / r) * g0), hi = f2bf((v[j][2 * e + 1] / r) * g1);
+        o[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      *(u32x4*)(out + packed_index(m, 8 * c, d)) = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ x, const float* __restrict__ gain,
+                                                     float eps, int d, int row0, float* __restrict__ out) {
+  const int m = blockIdx.x;
+  const float* xr = x + (int64_t)(row0 + m) * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) ss += xr[k] * xr[k];
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float r = sqrtf(tot / (float)d + eps);
+  for (int k = threadIdx.x; k < d; k += 256) out[(int64_t)m * d + k] = (xr[k] / r) * gain[k];
+}
+
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, float eps, int M, int d, int row0, void* out,
+                          hipStream_t st) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, (const uint16_t*)gain, eps, d, row0,
+                       (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_f32, dim3(M), dim3(256), 0, st, x, (const float*)gain, eps, d, row0, (float*)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Vocab partial record: (max, lowest argmax, second max, sum exp(l - max)).
+// ---------------------------------------------------------------------------
+struct Rec {
+  float mx;
+  int idx;
+  float mx2;
+  float sum;
+};
+__device__ __forceinline__ Rec rec_empty() { return Rec{-INFINITY, 0x7fffffff, -INFINITY, 0.f}; }
+__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
+  const bool a_top = a.mx > b.mx || (a.mx == b.mx && a.idx < b.idx);
+  const Rec& t = a_top ? a : b;
+  const Rec& o = a_top ? b : a;
+  Rec r;
+  r.mx = t.mx;
+  r.idx = t.idx;
+  r.mx2 = fmaxf(t.mx2, o.mx);
+  r.sum = t.sum + (o.mx == -INFINITY ? 0.f : o.sum * __expf(o.mx - t.mx));
+  return r;
+}
+__device__ __forceinline__ Rec rec_shfl_xor(const Rec& a, int o) {
+  Rec r;
+  r.mx = __shfl_xor(a.mx, o);
+  r.idx = __shfl_xor(a.idx, o);
+  r.mx2 = __shfl_xor(a.mx2, o);
+  r.sum = __shfl_xor(a.sum, o);
+  return r;
+}
+__device__ __forceinline__ float4 rec_pack(const Rec& a) { return make_float4(a.mx, __int_as_float(a.idx), a.mx2, a.sum); }
+__device__ __forceinline__ Rec rec_unpack(const float4& v) { return Rec{v.x, __float_as_int(v.y), v.z, v.w}; }
+
+// ---------------------------------------------------------------------------
+// Epilogues of the bf16 GEMM.  c[16] is a 32x32 C tile in the MFMA layout:
+// column m = tile row-of-activations (lane % 32), rows crow(r, lane / 32).
+// ---------------------------------------------------------------------------
+template <int EPI>
+__device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int mt, int lane, const EpiArgs& ea) {
+  const int h = lane >> 5;
+  const int m = mt * 32 + (lane & 31);
+  const bool valid = m < ea.M;
+  if constexpr (EPI == EPI_QKV) {
+    if (!valid) return;
+    const int slot = m / ea.slots.T, t = m % ea.slots.T;
+    const int seq = ea.slots.ids[slot];
+    const int pos = ea.kv.seq_len[seq] + t;
+    const int head = nt >> 2, s4 = nt & 3;
+    const int Hq = ea.Hq, Hkv = ea.kv.Hkv;
+    uint16_t* pool = (uint16_t*)ea.kv.pool;
+    const int page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + pos / kPageTokens];
+    const int pk = pos % kPageTokens;
+    uint16_t* kblk = nullptr;
+    uint16_t* vblk = nullptr;
+    if (head >= Hq) {
+      const int64_t base = (int64_t)page * ea.kv.page_elems + ea.kv.layer_off;
+      if (head < Hq + Hkv) kblk = pool + base + (int64_t)(head - Hq) * kPageTokens * kHd;
+      else vblk = pool + base + (int64_t)(Hkv + head - Hq - Hkv) * kPageTokens * kHd;
+    }
+#pragma unroll 2
+    for (int r = 0; r < 8; ++r) {
+      const int dl = 16 * s4 + crow(r, h);  // first-half dim; partner dim dl + 64 is c[r + 8]
+      float y1 = c[r], y2 = c[r + 8];
+      if (head < Hq + Hkv) {
+        const float cs = ea.rope_cos[(int64_t)pos * (kHd / 2) + dl];
+        const float sn = ea.rope_sin[(int64_t)pos * (kHd / 2) + dl];
+        const float x1 = y1, x2 = y2;
+        y1 = x1 * cs - x2 * sn;
+        y2 = x2 * cs + x1 * sn;
+      }
+      const uint16_t b1 = f2bf(y1), b2 = f2bf(y2);
+      if (head < Hq) {
+        uint16_t* q = ea.q_out + ((int64_t)m * Hq + head) * kHd;
+        q[dl] = b1;
+        q[dl + 64] = b2;
+      } else if (kblk) {
+        kblk[kv_k_index(pk, dl)] = b1;
+        kblk[kv_k_index(pk, dl + 64)] = b2;
+      } else {
+        vblk[kv_v_index(pk, dl)] = b1;
+        vblk[kv_v_index(pk, dl + 64)] = b2;
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    if (!valid) return;
+    float* xr = ea.x + (int64_t)m * ea.d + nt * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xr[crow(r, h)] += c[r];
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (!valid) return;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int f = 16 * nt + crow(r, h);
+      const float g = c[r], u = c[r + 8];
+      const float s = g / (1.f + expf(-g));
+      ea.h_out[packed_index(m, f, ea.F)] = f2bf(s * u);
+    }
+  } else {  // EPI_LOGITS
+    Rec a = rec_empty();
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+      const int n = nt * 32 + crow(r, h);
+      if (valid && ea.logits) ea.logits[(int64_t)m * ea.V + n] = c[r];
+      if (n != ea.mask_id) a = rec_merge(a, Rec{c[r], n, -INFINITY, 1.f});
+    }
+    const Rec b = rec_shfl_xor(a, 32);
+    a = rec_merge(a, b);
+    if (valid && h == 0) ea.records[(int64_t)m * ea.n_vtiles + nt] = rec_pack(a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny bf16 GEMM  Y[m, n] = sum_k X[m, k] W[n, k]  (fp32 accumulate).
+// grid (NT, ceil(MTILES / MT)); WAVES waves per workgroup.  Workgroup nt owns
+// the 32-row weight tile nt over the whole K range; its waves take WAVES
+// contiguous K ranges, streaming the packed weights once (1 KiB per wave per
+// load, non-temporal) and the activation tiles from L2.  The waves' partial
+// tiles are summed through LDS in wave order, so the summation order depends
+// only on (N, K, WAVES) -- never on the number of rows: every row's result is
+// independent of the batch it is computed in.
+// ---------------------------------------------------------------------------
+template <int EPI, int MT, int U, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
+                                                          const uint16_t* __restrict__ X, GemmShape g, EpiArgs ea) {
+  const int nt = blockIdx.x, mg = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int mt0 = mg * MT;
+  const int mcount = min(MT, g.MTILES - mt0);
+  const int per = (g.KB + WAVES - 1) / WAVES;
+  const int kb0 = min(g.KB, wave * per);
+  const int kb1 = min(g.KB, (wave + 1) * per);
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x16{0};
+
+  const u32x4* wp = (const u32x4*)W + (int64_t)nt * g.KB * 64 + lane;
+  const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
+  int kb = kb0;
+  for (; kb + U <= kb1; kb += U) {
+    u32x4 wv[U];
+    u32x4 xv[MT][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) wv[u] = __builtin_nontemporal_load(wp + (int64_t)(kb + u) * 64);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      if (i < mcount) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) xv[i][u] = xp[((int64_t)i * g.KB + kb + u) * 64];
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        if (i < mcount) acc[i] = mfma32(wv[u], xv[i][u], acc[i]);
+  }
+  for (; kb < kb1; ++kb) {
+    const u32x4 wv = __builtin_nontemporal_load(wp + (int64_t)kb * 64);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      if (i < mcount) acc[i] = mfma32(wv, xp[((int64_t)i * g.KB + kb) * 64], acc[i]);
+  }
+
+  // reduction over the waves through LDS, one activation tile at a time
+  __shared__ float red[WAVES][16][64];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (i >= mcount) break;
+    if (i > 0) __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[i][r];
+    __syncthreads();
+    if (wave == 0) {
+      float c[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = red[0][r][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += red[w][r][lane];
+        c[r] = v;
+      }
+      gemm_epilogue<EPI>(c, nt, mt0 + i, lane, ea);
+    }
+  }
+}
+
+// Waves per workgroup: enough to keep ~16 KiB of weights in flight per wave
+// when the matrix has few 32-row tiles (a function of N and K only).
+static int gemm_waves(const GemmShape& g) {
+  if (g.NT >= 1024) return 4;
+  if (g.NT >= 384) return g.KB >= 128 ? 8 : 4;
+  return g.KB >= 256 ? 16 : (g.KB >= 64 ? 8 : 4);
+}
+
+template <int EPI, int WAVES>
+static void launch_gemm_w(const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea, hipStream_t st) {
+  const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
+  const dim3 grd(g.NT, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
+  // 16-wave workgroups have 128 registers per lane: smaller load batches
+  constexpr int U1 = WAVES >= 16 ? 8 : 16, U2 = WAVES >= 16 ? 4 : 8, U4 = WAVES >= 16 ? 2 : 4;
+  if (MT == 1) hipLaunchKernelGGL((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  else if (MT == 2) hipLaunchKernelGGL((k_gemm_bf16<EPI, 2, U2, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  else hipLaunchKernelGGL((k_gemm_bf16<EPI, 4, U4, WAVES>), grd, blk, 0, st, W, X, g, ea);
+}
+
+template <int EPI>
+static hipError_t launch_gemm_epi(const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
+                                  hipStream_t st) {
+  int waves = gemm_waves(g);
+  // the RoPE/KV-write and vocab epilogues need more than 128 registers per lane
+  if ((EPI == EPI_QKV || EPI == EPI_LOGITS) && waves > 8) waves = 8;
+  switch (waves) {
+    case 16:
+      if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU) launch_gemm_w<EPI, 16>(W, X, g, ea, st);
+      break;
+    case 8: launch_gemm_w<EPI, 8>(W, X, g, ea, st); break;
+    default: launch_gemm_w<EPI, 4>(W, X, g, ea, st); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
+                            hipStream_t st) {
+  switch (epi) {
+    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(W, X, g, ea, st);
+    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(W, X, g, ea, st);
+    case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(W, X, g, ea, st);
+    default: return launch_gemm_epi<EPI_LOGITS>(W, X, g, ea, st);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block attention, bf16, head_dim 128, over the paged cache.
+// grid (splits, Hkv, slots), 4 waves.  Workgroup (sp, g, slot) covers the
+// absolute key range [sp*256, sp*256+256) of KV head g for every query column
+// (q head of the group, block row); wave w takes query tiles w, w+4, ...
+// S^T = K Q^T on MFMA (keys x query columns), an online softmax per column,
+// then O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts so the
+// product keeps ~16 bits of P.  Partials (O, max, sum) go to the workspace;
+// the combine kernel merges the splits in split order.  Masked keys add exact
+// zeros, so a row's result does not depend on how many rows the block has.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
+  constexpr int kPagesPerSplit = kAttnSplitKeys / kPageTokens;
+  constexpr int kBlockVec = kPageTokens * kHd / 8;  // 16-byte vectors in one K (or V) page block
+  __shared__ u32x4 sK[kPagesPerSplit][kBlockVec];
+  __shared__ u32x4 sV[kPagesPerSplit][kBlockVec];
+  const int sp = blockIdx.x, g = blockIdx.y, slot = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int seq = a.slots.ids[slot];
+  const int T = a.slots.T;
+  const int n = a.kv.seq_len[seq];
+  const int nkeys = n + T;
+  const int j0 = sp * kAttnSplitKeys;
+  if (j0 >= nkeys) return;
+  const int j1 = min(j0 + kAttnSplitKeys, nkeys);
+  const int Hkv = a.kv.Hkv;
+  const int G = a.Hq / Hkv;
+  const int nq = G * T;
+  const int nqt = (nq + 31) >> 5;
+  const uint16_t* pool = (const uint16_t*)a.kv.pool;
+  const int* ptab = a.kv.page_table + (int64_t)seq * a.kv.max_pages;
+  const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
+
+  // stage this split's K and V page blocks in LDS: all loads issued before any store
+  const int npages = (j1 - j0 + kPageTokens - 1) / kPageTokens;
+  {
+    constexpr int kPer = kPagesPerSplit * kBlockVec / 256;  // vectors per thread per block kind
+    u32x4 bk[kPer], bv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      const int p = idx / kBlockVec, o = idx % kBlockVec;
+      if (p < npages) {
+        const int64_t pb = (int64_t)ptab[j0 / kPageTokens + p] * a.kv.page_elems + a.kv.layer_off;
+        bk[i] = ((const u32x4*)(pool + pb + (int64_t)g * kPageTokens * kHd))[o];
+        bv[i] = ((const u32x4*)(pool + pb + (int64_t)(Hkv + g) * kPageTokens * kHd))[o];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      const int p = idx / kBlockVec, o = idx % kBlockVec;
+      if (p < npages) {
+        sK[p][o] = bk[i];
+        sV[p][o] = bv[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int qt = wave; qt < nqt; qt += 4) {
+    const int c = qt * 32 + (lane & 31);
+    const bool cval = c < nq;
+    const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
+    const int head = g * G + hl;
+    const int qpos = n + t;
+    u32x4 qop[8];
+    {
+      const u32x4* qp = (const u32x4*)(a.q + ((int64_t)(slot * T + t) * a.Hq + head) * kHd);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) qop[kb] = cval ? qp[2 * kb + h] : u32x4{0, 0, 0, 0};
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32x16{0};
+
+    for (int jt = j0; jt < j1; jt += 32) {
+      const int pi = (jt - j0) / kPageTokens;
+      const int kt = (jt % kPageTokens) >> 5;
+      f32x16 sacc = f32x16{0};
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) sacc = mfma32(sK[pi][(kt * 8 + kb) * 64 + lane], qop[kb], sacc);
+      float sv[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jt + crow(r, h);
+        const bool vis = cval && j < nkeys && (j < n || a.mode == BIDIR || j <= qpos);
+        sv[r] = vis ? sacc[r] * a.scale : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = (sv[r] == -INFINITY) ? 0.f : __expf(sv[r] - m_new);
+        psum += sv[r];
+      }
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+#pragma unroll
+      for (int ka = 0; ka < 2; ++ka) {
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = sv[8 * ka + e];
+          hi[e] = f2bf(p);
+          lo[e] = f2bf(p - bf2f(hi[e]));
+        }
+        u32x4 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          phi[e] = (uint32_t)hi[2 * e] | ((uint32_t)hi[2 * e + 1] << 16);
+          plo[e] = (uint32_t)lo[2 * e] | ((uint32_t)lo[2 * e + 1] << 16);
+        }
+        const int kbv = ((jt % kPageTokens) >> 4) + ka;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x4 vop = sV[pi][(dt * (kPageTokens / 16) + kbv) * 64 + lane];
+          o[dt] = mfma32(vop, phi, o[dt]);
+          o[dt] = mfma32(vop, plo, o[dt]);
+        }
+      }
+    }
+    if (cval) {
+      float* op = a.opart + base_idx * kHd * a.nq_pad;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) op[(int64_t)(dt * 32 + crow(r, h)) * a.nq_pad + c] = o[dt][r];
+      if (h == 0) {
+        a.mlpart[(base_idx * 2 + 0) * a.nq_pad + c] = m_run;
+        a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = l_run;
+      }
+    }
+  }
+}
+
+// o = sum_s w_s O_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s); rounded to bf16.
+__global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
+  const int g = blockIdx.y, slot = blockIdx.z;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int c = idx % a.nq_pad, d = idx / a.nq_pad;
+  const int T = a.slots.T;
+  const int Hkv = a.kv.Hkv, G = a.Hq / Hkv, nq = G * T;
+  if (d >= kHd || c >= nq) return;
+  const int seq = a.slots.ids[slot];
+  const int nkeys = a.kv.seq_len[seq] + T;
+  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  const int64_t b0 = ((int64_t)slot * Hkv + g) * a.max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.mlpart[((b0 + s) * 2) * a.nq_pad + c]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < nsp; ++s) {
+    const float ms = a.mlpart[((b0 + s) * 2) * a.nq_pad + c];
+    if (ms == -INFINITY) continue;
+    const float w = __expf(ms - M);
+    L += w * a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c];
+    acc += w * a.opart[((b0 + s) * kHd + d) * a.nq_pad + c];
+  }
+  const float o = acc / L;
+  const int hl = c / T, t = c % T;
+  const int64_t m = (int64_t)slot * T + t;
+  const int64_t k = (int64_t)(g * G + hl) * kHd + d;
+  const int64_t K = (int64_t)a.Hq * kHd;
+  if (a.out_packed) a.out[packed_index(m, k, K)] = f2bf(o);
+  else a.out[m * K + k] = f2bf(o);
+}
+
+hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st) {
+  hipLaunchKernelGGL(k_attn_bf16, dim3(grid_splits, a.kv.Hkv, a.slots.n_seq), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {
+  const int n = a.nq_pad * kHd;
+  hipLaunchKernelGGL(k_attn_combine_bf16, dim3((n + 255) / 256, a.kv.Hkv, a.slots.n_seq), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.
+__global__ void k_attn_pack_kv(int Hkv, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_keys,
+                               const int* __restrict__ pages, uint16_t* __restrict__ pool) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_keys * Hkv * kHd) return;
+  const int d = i % kHd, g = (i / kHd) % Hkv, j = (int)(i / ((int64_t)kHd * Hkv));
+  const int64_t page_elems = 2LL * Hkv * kPageTokens * kHd;
+  const int page = pages[j / kPageTokens], pk = j % kPageTokens;
+  uint16_t* pb = pool + (int64_t)page * page_elems;
+  pb[(int64_t)g * kPageTokens * kHd + kv_k_index(pk, d)] = k[i];
+  pb[(int64_t)(Hkv + g) * kPageTokens * kHd + kv_v_index(pk, d)] = v[i];
+}
+hipError_t launch_attn_pack_kv(int Hkv, const uint16_t* k, const uint16_t* v, int n_keys, const int* pages,
+                               uint16_t* pool, hipStream_t st) {
+  const int64_t n = (int64_t)n_keys * Hkv * kHd;
+  hipLaunchKernelGGL(k_attn_pack_kv, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Hkv, k, v, n_keys, pages,
+                     pool);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-row selection: merge a row's vocab records (fixed order) into
+// tok = lowest argmax over non-MASK ids, conf = 1 / sum exp(l - max) and the
+// top-2 margin.  One workgroup per row; records loaded 8 per thread at a time.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_select_rows(const float4* __restrict__ records, int n_vtiles,
+                                                     int* __restrict__ tok, float* __restrict__ conf,
+                                                     float* __restrict__ margin) {
+  const int m = blockIdx.x;
+  const float4* rr = records + (int64_t)m * n_vtiles;
+  Rec a = rec_empty();
+  for (int base = 0; base < n_vtiles; base += 256 * 8) {
+    float4 buf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int vt = base + threadIdx.x + 256 * j;
+      buf[j] = vt < n_vtiles ? rr[vt] : rec_pack(rec_empty());
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = rec_merge(a, rec_unpack(buf[j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = rec_merge(a, rec_shfl_xor(a, o));
+  __shared__ float4 part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = rec_pack(a);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Rec r = rec_unpack(part[0]);
+    for (int w = 1; w < 4; ++w) r = rec_merge(r, rec_unpack(part[w]));
+    tok[m] = r.idx;
+    conf[m] = 1.f / r.sum;
+    margin[m] = r.mx - r.mx2;
+  }
+}
+
+// The mode rules on a sequence's rows.  One workgroup (one thread) per slot.
+__global__ void k_finish_mode(FinishArgs f) {
+  const int slot = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int T = f.T;
+  const int r0 = slot * T;
+  if (f.mode == FIN_NEXT) {
+    if (slot == 0) f.next[0] = f.tok[r0 + T - 1];
+  } else if (f.mode == FIN_DRAFT) {
+    f.block[r0] = f.anchor[slot];
+    for (int j = 1; j < T; ++j) f.block[r0 + j] = f.tok[r0 + j];
+  } else if (f.mode == FIN_VERIFY) {
+    int k = 0;
+    while (k + 1 <= T - 1 && f.block[r0 + k + 1] == f.tok[r0 + k]) ++k;
+    for (int j = 0; j < T; ++j) f.ar_out[r0 + j] = f.tok[r0 + j];
+    f.accept[slot] = k + 1;
+  } else {  // FIN_DIFFUSE
+    int best = -1, n_m = 0, n_u = 0;
+    for (int i = 0; i < T; ++i)
+      if (f.block[r0 + i] == f.mask_id) {
+        ++n_m;
+        if (best < 0 || f.conf[r0 + i] > f.conf[r0 + best]) best = i;
+      }
+    for (int i = 0; i < T; ++i) {
+      if (f.conf_out) f.conf_out[r0 + i] = f.conf[r0 + i];
+      if (f.block[r0 + i] != f.mask_id) continue;
+      if (f.force_all || i == best || f.conf[r0 + i] > f.tau) {
+        f.block[r0 + i] = f.tok[r0 + i];
+        ++n_u;
+      }
+    }
+    f.n_masked[slot] = n_m - n_u;
+  }
+}
+
+hipError_t launch_finish(const FinishArgs& f, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_rows, dim3(f.M), dim3(256), 0, st, f.records, f.n_vtiles, f.tok, f.conf, f.margin);
+  hipLaunchKernelGGL(k_finish_mode, dim3(f.slots.n_seq), dim3(64), 0, st, f);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (tiny decoder): plain VALU kernels, one output per thread, each
+// reduction in a fixed sequential order.
+// ---------------------------------------------------------------------------
+__global__ void k_gemm_f32(const float* __restrict__ X, const float* __restrict__ W, int M, int N, int K,
+                           float* __restrict__ Y) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x, m = blockIdx.y;
+  if (n >= N) return;
+  const float* x = X + (int64_t)m * K;
+  const float* w = W + (int64_t)n * K;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) acc = fmaf(x[k], w[k], acc);
+  Y[(int64_t)m * N + n] = acc;
+}
+hipError_t launch_gemm_f32(const float* X, const float* W, int M, int N, int K, float* Y, hipStream_t st) {
+  hipLaunchKernelGGL(k_gemm_f32, dim3((N + 127) / 128, M), dim3(128), 0, st, X, W, M, N, K, Y);
+  return hipGetLastError();
+}
+
+// Y [M][(Hq + 2 Hkv) hd] -> RoPE'd q [M][Hq][hd], K/V rows into the pages.
+__global__ void k_qkv_post_f32(const float* __restrict__ Y, EpiArgs ea, int hd) {
+  const int m = blockIdx.x;
+  const int Hq = ea.Hq, Hkv = ea.kv.Hkv, half = hd / 2;
+  const int ncols = (Hq + 2 * Hkv) * hd;
+  const int slot = m / ea.slots.T, t = m % ea.slots.T;
+  const int seq = ea.slots.ids[slot];
+  const int pos = ea.kv.seq_len[seq] + t;
+  const int page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + pos / kPageTokens];
+  const int pk = pos % kPageTokens;
+  float* pool = (float*)ea.kv.pool;
+  const int64_t pbase = (int64_t)page * ea.kv.page_elems + ea.kv.layer_off;
+  const float* y = Y + (int64_t)m * ncols;
+  for (int i = threadIdx.x; i < (Hq + 2 * Hkv) * half; i += blockDim.x) {
+    const int head = i / half, dl = i % half;
+    float v1 = y[head * hd + dl], v2 = y[head * hd + dl + half];
+    if (head < Hq + Hkv) {
+      const float cs = ea.rope_cos[(int64_t)pos * half + dl], sn = ea.rope_sin[(int64_t)pos * half + dl];
+      const float x1 = v1, x2 = v2;
+      v1 = x1 * cs - x2 * sn;
+      v2 = x2 * cs + x1 * sn;
+    }
+    if (head < Hq) {
+      float* q = (float*)ea.q_out + ((int64_t)m * Hq + head) * hd;
+      q[dl] = v1;
+      q[dl + half] = v2;
+    } else {
+      const int blk = head - Hq;  // K heads 0..Hkv-1, then V heads
+      float* dst = pool + pbase + ((int64_t)blk * kPageTokens + pk) * hd;
+      dst[dl] = v1;
+      dst[dl + half] = v2;
+    }
+  }
+}
+hipError_t launch_qkv_post_f32(const float* Y, const EpiArgs& ea, int hd, hipStream_t st) {
+  hipLaunchKernelGGL(k_qkv_post_f32, dim3(ea.M), dim3(128), 0, st, Y, ea, hd);
+  return hipGetLastError();
+}
+
+// One thread per (row, q head); keys visited in ascending order.
+__global__ void k_attn_f32(const float* __restrict__ q, KvView kv, Slots sl, int Hq, int mode,
+                           float* __restrict__ out) {
+  const int m = blockIdx.x;
+  const int head = threadIdx.x;
+  if (head >= Hq) return;
+  const int hd = kv.hd, Hkv = kv.Hkv;
+  const int g = head * Hkv / Hq;
+  const int slot = m / sl.T, t = m % sl.T;
+  const int seq = sl.ids[slot];
+  const int n = kv.seq_len[seq];
+  const int last = (mode == BIDIR) ? n + sl.T - 1 : n + t;
+  const float* pool = (const float*)kv.pool;
+  const int* ptab = kv.page_table + (int64_t)seq * kv.max_pages;
+  const float* qv = q + ((int64_t)m * Hq + head) * hd;
+  const float scale = 1.f / sqrtf((float)hd);
+  float mx = -INFINITY;
+  for (int j = 0; j <= last; ++j) {
+    const float* kr = pool + (int64_t)ptab[j / kPageTokens] * kv.page_elems + kv.layer_off +
+                      ((int64_t)g * kPageTokens + j % kPageTokens) * hd;
+    float s = 0.f;
+    for (int d = 0; d < hd; ++d) s = fmaf(qv[d], kr[d], s);
+    mx = fmaxf(mx, s * scale);
+  }
+  float acc[128];
+  for (int d = 0; d < hd; ++d) acc[d] = 0.f;
+  float sum = 0.f;
+  for (int j = 0; j <= last; ++j) {
+    const int64_t pb = (int64_t)ptab[j / kPageTokens] * kv.page_elems + kv.layer_off;
+    const float* kr = pool + pb + ((int64_t)g * kPageTokens + j % kPageTokens) * hd;
+    const float* vr = pool + pb + ((int64_t)(Hkv + g) * kPageTokens + j % kPageTokens) * hd;
+    float s = 0.f;
+    for (int d = 0; d < hd; ++d) s = fmaf(qv[d], kr[d], s);
+    const float p = expf(s * scale - mx);
+    sum += p;
+    for (int d = 0; d < hd; ++d) acc[d] = fmaf(p, vr[d], acc[d]);
+  }
+  float* o = out + ((int64_t)m * Hq + head) * hd;
+  for (int d = 0; d < hd; ++d) o[d] = acc[d] / sum;
+}
+hipError_t launch_attention_f32(const float* q, const KvView& kv, const Slots& sl, int Hq, int mode, float* out,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(k_attn_f32, dim3(sl.n_seq * sl.T), dim3(64), 0, st, q, kv, sl, Hq, mode, out);
+  return hipGetLastError();
+}
+
+__global__ void k_resid_f32(const float* __restrict__ Y, float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] += Y[i];
+}
+hipError_t launch_resid_f32(const float* Y, float* x, int M, int d, hipStream_t st) {
+  const int64_t n = (int64_t)M * d;
+  hipLaunchKernelGGL(k_resid_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Y, x, n);
+  return hipGetLastError();
+}
+
+__global__ void k_swiglu_f32(const float* __restrict__ Y, float* __restrict__ hout, int M, int F) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * F) return;
+  const int64_t m = i / F, f = i % F;
+  const float g = Y[m * 2 * F + f], u = Y[m * 2 * F + F + f];
+  hout[i] = g / (1.f + expf(-g)) * u;
+}
+hipError_t launch_swiglu_f32(const float* Y, float* h, int M, int F, hipStream_t st) {
+  const int64_t n = (int64_t)M * F;
+  hipLaunchKernelGGL(k_swiglu_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Y, h, M, F);
+  return hipGetLastError();
+}
+
+__global__ void k_logit_records_f32(const float* __restrict__ Y, EpiArgs ea) {
+  const int m = blockIdx.y;
+  const int vt = blockIdx.x * blockDim.x + threadIdx.x;
+  if (vt >= ea.n_vtiles) return;
+  Rec a = rec_empty();
+  for (int i = 0; i < 32; ++i) {
+    const int n = vt * 32 + i;
+    if (n >= ea.V) break;
+    const float v = Y[(int64_t)m * ea.V + n];
+    if (ea.logits) ea.logits[(int64_t)m * ea.V + n] = v;
+    if (n != ea.mask_id) a = rec_merge(a, Rec{v, n, -INFINITY, 1.f});
+  }
+  ea.records[(int64_t)m * ea.n_vtiles + vt] = rec_pack(a);
+}
+hipError_t launch_logit_records_f32(const float* Y, const EpiArgs& ea, hipStream_t st) {
+  hipLaunchKernelGGL(k_logit_records_f32, dim3((ea.n_vtiles + 63) / 64, ea.M), dim3(64), 0, st, Y, ea);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Bookkeeping: write up to 64 ints given by value (page-table rows, lengths).
+// ---------------------------------------------------------------------------
+struct IntVals {
+  int v[64];
+};
+__global__ void k_set_ints(int* dst, IntVals vals, int n) {
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = vals.v[threadIdx.x];
+}
+hipError_t launch_set_ints(int* dst, const int* vals, int n, hipStream_t st) {
+  IntVals iv;
+  for (int i = 0; i < n && i < 64; ++i) iv.v[i] = vals[i];
+  hipLaunchKernelGGL(k_set_ints, dim3(1), dim3(64), 0, st, dst, iv, n);
+  return hipGetLastError();
+}
+
+}  // namespace sdm
