@@ -68,7 +68,7 @@ typedef enum { SDM_CAUSAL = 0, SDM_BIDIR = 1 } sdm_attn_mode;
  *   head_dim.  n_q_heads must be a multiple of n_kv_heads.  mask_id is the
  *   reserved MASK token (vocab - 1 in every shipped shape).  page_tokens must
  *   be 64.  max_rows bounds the rows of one forward (n_seq * block, or a
- *   prefill chunk); max_context bounds a sequence's length (prompt + output
+ *   prefill chunk); max_context (<= 65536) bounds a sequence's length (prompt + output
  *   + one block). */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, mask_id;
@@ -192,7 +192,7 @@ sdm_status sdm_timing_stop(sdm_model* m, int64_t* launches, double* total_ms, do
  * out: d_out [T, Hq, hd] bf16, softmax(q.k / sqrt(hd)) over the visible keys
  *     applied to v; key j visible to block row i iff j < n_prefix or
  *     (j < n_prefix + T and (mode == SDM_BIDIR or j <= n_prefix + i)).
- * hd must be 128, Hq a multiple of Hkv, 1 <= T <= 4096.  Every slot of the
+ * hd must be 128, Hq a multiple of Hkv, 1 <= T <= 4096, n_prefix + T <= 65536.  Every slot of the
  * pages that hold keys [0, n_prefix + T) must contain finite values (zero the
  * pool once): keys past the end of the last 32-key tile are read and given
  * probability 0. */

@@ -13,7 +13,7 @@ constexpr int kMaxSlots = 64;          // sequences in one forward
 constexpr int kHd = 128;               // bf16 path head dim
 
 enum Mode { CAUSAL = 0, BIDIR = 1 };
-enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3 };
 enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1 };
 
@@ -79,12 +79,36 @@ struct EpiArgs {
   int n_vtiles;
   float* logits;         // LOGITS: optional [M][V]
   int V, mask_id;
+  float* part;           // PARTIAL: [S][rows][d] fp32 split-K partials
+  int64_t part_stride;   // elements between splits
 };
 
 struct GemmShape {
   int NT, KB;            // 32-row tiles of W, 16-column blocks of K
   int MTILES;            // 32-row tiles of the activations
+  int S;                 // workgroups splitting K (EPI_PARTIAL only)
+  int WAVES;             // waves per workgroup, splitting the workgroup's K range
 };
+
+// Launch configuration of a weight matrix: a function of the matrix shape and
+// its epilogue only (never of the number of rows), so that the summation order
+// -- and therefore every row's result -- does not depend on the batch.
+// Matrices whose outputs are summed into the residual stream (EPI_PARTIAL) are
+// split over S workgroups along K until the grid covers the chip; each split
+// writes an fp32 partial that the following RMSNorm adds in split order.
+inline GemmShape gemm_config(int epi, int N, int K, int rows) {
+  GemmShape g;
+  g.NT = N / 32;
+  g.KB = K / 16;
+  g.MTILES = (rows + 31) / 32;
+  g.S = 1;
+  if (epi == EPI_PARTIAL)
+    while (g.NT * g.S < 256 && g.KB % (2 * g.S) == 0 && g.KB / (2 * g.S) >= 64 && g.S < 4) g.S *= 2;
+  if (g.NT >= 1024) g.WAVES = 4;
+  else if (g.KB / g.S >= 128) g.WAVES = 8;
+  else g.WAVES = 4;
+  return g;
+}
 
 struct AttnArgs {
   const uint16_t* q;     // [rows][Hq][hd] (row-major)
@@ -121,8 +145,8 @@ hipError_t launch_pack(int dtype, int kind, const void* src, const void* src2, v
                        int head_dim, hipStream_t st);
 hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* tokens, int tok_src, const int* anchor,
                         int M, int T, int mask_id, float* x, hipStream_t st);
-hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, float eps, int M, int d, int row0,
-                          void* out, hipStream_t st);
+hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
+                          float eps, int M, int d, int row0, void* out, hipStream_t st);
 hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
                             hipStream_t st);
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st);

@@ -127,10 +127,12 @@ hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* token
 // ---------------------------------------------------------------------------
 constexpr int kNormChunks = 4;  // chunks of 8 features per thread: d <= 8192
 
-__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* __restrict__ x, const uint16_t* __restrict__ gain,
-                                                      float eps, int d, int row0, uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, const float* __restrict__ part,
+                                                      int nparts, int64_t part_stride,
+                                                      const uint16_t* __restrict__ gain, float eps, int d, int row0,
+                                                      uint16_t* __restrict__ out) {
   const int m = blockIdx.x;
-  const float* xr = x + (int64_t)(row0 + m) * d;
+  float* xr = x + (int64_t)(row0 + m) * d;
   const int nch = d >> 3;
   float v[kNormChunks][8];
   float ss = 0.f;
@@ -141,15 +143,33 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* __restrict__ 
       const float4 a = ((const float4*)xr)[2 * c], b = ((const float4*)xr)[2 * c + 1];
       v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
       v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+      if (nparts > 0) {
+        // residual += sum of the split-K partials of the preceding projection (split order)
+        float pv[8];
+        const float* pr = part + (int64_t)(row0 + m) * d + 8 * c;
+        {
+          const float4 pa = ((const float4*)pr)[0], pb = ((const float4*)pr)[1];
+          pv[0] = pa.x; pv[1] = pa.y; pv[2] = pa.z; pv[3] = pa.w; pv[4] = pb.x; pv[5] = pb.y; pv[6] = pb.z; pv[7] = pb.w;
+        }
+        for (int sp = 1; sp < nparts; ++sp) {
+          const float4 pa = ((const float4*)(pr + sp * part_stride))[0], pb = ((const float4*)(pr + sp * part_stride))[1];
+          pv[0] += pa.x; pv[1] += pa.y; pv[2] += pa.z; pv[3] += pa.w;
+          pv[4] += pb.x; pv[5] += pb.y; pv[6] += pb.z; pv[7] += pb.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] += pv[e];
+        ((float4*)xr)[2 * c] = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+        ((float4*)xr)[2 * c + 1] = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
     }
   }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __shared__ float wsum[4];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   const float r = sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int j = 0; j < kNormChunks; ++j) {
@@ -183,11 +203,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ x
   for (int k = threadIdx.x; k < d; k += 256) out[(int64_t)m * d + k] = (xr[k] / r) * gain[k];
 }
 
-hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, float eps, int M, int d, int row0, void* out,
-                          hipStream_t st) {
+hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
+                          float eps, int M, int d, int row0, void* out, hipStream_t st) {
   if (dtype == 1)
-    hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, (const uint16_t*)gain, eps, d, row0,
-                       (uint16_t*)out);
+    hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, part, nparts, part_stride,
+                       (const uint16_t*)gain, eps, d, row0, (uint16_t*)out);
   else
     hipLaunchKernelGGL(k_rmsnorm_f32, dim3(M), dim3(256), 0, st, x, (const float*)gain, eps, d, row0, (float*)out);
   return hipGetLastError();
@@ -228,36 +248,70 @@ __device__ __forceinline__ Rec rec_unpack(const float4& v) { return Rec{v.x, __f
 // ---------------------------------------------------------------------------
 // Epilogues of the bf16 GEMM.  c[16] is a 32x32 C tile in the MFMA layout:
 // column m = tile row-of-activations (lane % 32), rows crow(r, lane / 32).
+// EpiPre holds the epilogue's inputs that do not depend on the product (RoPE
+// cos/sin, the KV page, the residual values); the GEMM loads it before its K
+// loop so those loads' latency hides behind the weight stream.
 // ---------------------------------------------------------------------------
+struct EpiPre {
+  float v[16];
+  int pos, page;
+};
+
 template <int EPI>
-__device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int mt, int lane, const EpiArgs& ea) {
+__device__ __forceinline__ void epi_preload(EpiPre& p, int nt, int mt, int lane, const EpiArgs& ea) {
+  const int h = lane >> 5;
+  const int m = mt * 32 + (lane & 31);
+  if (m >= ea.M) return;
+  if constexpr (EPI == EPI_QKV) {
+    const int slot = m / ea.slots.T, t = m % ea.slots.T;
+    const int seq = ea.slots.ids[slot];
+    p.pos = ea.kv.seq_len[seq] + t;
+    p.page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + p.pos / kPageTokens];
+    const int head = nt >> 2, s4 = nt & 3;
+    if (head < ea.Hq + ea.kv.Hkv) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int dl = 16 * s4 + crow(r, h);
+        p.v[r] = ea.rope_cos[(int64_t)p.pos * (kHd / 2) + dl];
+        p.v[8 + r] = ea.rope_sin[(int64_t)p.pos * (kHd / 2) + dl];
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const float* xr = ea.x + (int64_t)m * ea.d + nt * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p.v[r] = xr[crow(r, h)];
+  }
+}
+
+template <int EPI, bool PRE>
+__device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int mt, int lane, const EpiArgs& ea,
+                                              const EpiPre& pre_in) {
   const int h = lane >> 5;
   const int m = mt * 32 + (lane & 31);
   const bool valid = m < ea.M;
   if constexpr (EPI == EPI_QKV) {
     if (!valid) return;
-    const int slot = m / ea.slots.T, t = m % ea.slots.T;
-    const int seq = ea.slots.ids[slot];
-    const int pos = ea.kv.seq_len[seq] + t;
+    EpiPre pre_local;
+    if constexpr (!PRE) epi_preload<EPI_QKV>(pre_local, nt, mt, lane, ea);
+    const EpiPre& pre = PRE ? pre_in : pre_local;
+    const int pos = pre.pos;
     const int head = nt >> 2, s4 = nt & 3;
     const int Hq = ea.Hq, Hkv = ea.kv.Hkv;
     uint16_t* pool = (uint16_t*)ea.kv.pool;
-    const int page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + pos / kPageTokens];
     const int pk = pos % kPageTokens;
     uint16_t* kblk = nullptr;
     uint16_t* vblk = nullptr;
     if (head >= Hq) {
-      const int64_t base = (int64_t)page * ea.kv.page_elems + ea.kv.layer_off;
+      const int64_t base = (int64_t)pre.page * ea.kv.page_elems + ea.kv.layer_off;
       if (head < Hq + Hkv) kblk = pool + base + (int64_t)(head - Hq) * kPageTokens * kHd;
       else vblk = pool + base + (int64_t)(Hkv + head - Hq - Hkv) * kPageTokens * kHd;
     }
-#pragma unroll 2
+#pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int dl = 16 * s4 + crow(r, h);  // first-half dim; partner dim dl + 64 is c[r + 8]
       float y1 = c[r], y2 = c[r + 8];
       if (head < Hq + Hkv) {
-        const float cs = ea.rope_cos[(int64_t)pos * (kHd / 2) + dl];
-        const float sn = ea.rope_sin[(int64_t)pos * (kHd / 2) + dl];
+        const float cs = pre.v[r], sn = pre.v[8 + r];
         const float x1 = y1, x2 = y2;
         y1 = x1 * cs - x2 * sn;
         y2 = x2 * cs + x1 * sn;
@@ -278,8 +332,19 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
   } else if constexpr (EPI == EPI_RESID) {
     if (!valid) return;
     float* xr = ea.x + (int64_t)m * ea.d + nt * 32;
+    if constexpr (PRE) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xr[crow(r, h)] += c[r];
+      for (int r = 0; r < 16; ++r) xr[crow(r, h)] = pre_in.v[r] + c[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xr[crow(r, h)] += c[r];
+    }
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    if (!valid) return;
+    // rows crow(4j + i, h) = 8j + 4h + i: four contiguous floats per j
+    float* pr = ea.part + (int64_t)blockIdx.y * ea.part_stride + (int64_t)m * ea.d + nt * 32 + 4 * h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(float4*)(pr + 8 * j) = make_float4(c[4 * j], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]);
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (!valid) return;
 #pragma unroll
@@ -316,17 +381,23 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
 template <int EPI, int MT, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, GemmShape g, EpiArgs ea) {
-  const int nt = blockIdx.x, mg = blockIdx.y;
+  const int nt = blockIdx.x, sk = blockIdx.y, mg = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int mt0 = mg * MT;
   const int mcount = min(MT, g.MTILES - mt0);
-  const int per = (g.KB + WAVES - 1) / WAVES;
-  const int kb0 = min(g.KB, wave * per);
-  const int kb1 = min(g.KB, (wave + 1) * per);
+  const int kbs = g.KB / g.S;  // this workgroup's K range: [sk * kbs, (sk + 1) * kbs)
+  const int per = (kbs + WAVES - 1) / WAVES;
+  const int kb0 = sk * kbs + min(kbs, wave * per);
+  const int kb1 = sk * kbs + min(kbs, (wave + 1) * per);
 
   f32x16 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x16{0};
+
+  EpiPre pre;
+  if constexpr (MT == 1) {
+    if (wave == 0) epi_preload<EPI>(pre, nt, mt0, lane, ea);
+  }
 
   const u32x4* wp = (const u32x4*)W + (int64_t)nt * g.KB * 64 + lane;
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
@@ -373,43 +444,28 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
         for (int w = 1; w < WAVES; ++w) v += red[w][r][lane];
         c[r] = v;
       }
-      gemm_epilogue<EPI>(c, nt, mt0 + i, lane, ea);
+      if constexpr (MT == 1) gemm_epilogue<EPI, true>(c, nt, mt0, lane, ea, pre);
+      else gemm_epilogue<EPI, false>(c, nt, mt0 + i, lane, ea, pre);
     }
   }
-}
-
-// Waves per workgroup: enough to keep ~16 KiB of weights in flight per wave
-// when the matrix has few 32-row tiles (a function of N and K only).
-static int gemm_waves(const GemmShape& g) {
-  if (g.NT >= 1024) return 4;
-  if (g.NT >= 384) return g.KB >= 128 ? 8 : 4;
-  return g.KB >= 256 ? 16 : (g.KB >= 64 ? 8 : 4);
 }
 
 template <int EPI, int WAVES>
 static void launch_gemm_w(const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea, hipStream_t st) {
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
-  const dim3 grd(g.NT, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
-  // 16-wave workgroups have 128 registers per lane: smaller load batches
-  constexpr int U1 = WAVES >= 16 ? 8 : 16, U2 = WAVES >= 16 ? 4 : 8, U4 = WAVES >= 16 ? 2 : 4;
+  const dim3 grd(g.NT, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
+  // split-K partial GEMMs stream with 8-deep batches (more waves resident per SIMD)
+  constexpr int U1 = EPI == EPI_PARTIAL ? 8 : 16;
   if (MT == 1) hipLaunchKernelGGL((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, g, ea);
-  else if (MT == 2) hipLaunchKernelGGL((k_gemm_bf16<EPI, 2, U2, WAVES>), grd, blk, 0, st, W, X, g, ea);
-  else hipLaunchKernelGGL((k_gemm_bf16<EPI, 4, U4, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  else if (MT == 2) hipLaunchKernelGGL((k_gemm_bf16<EPI, 2, 8, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  else hipLaunchKernelGGL((k_gemm_bf16<EPI, 4, 4, WAVES>), grd, blk, 0, st, W, X, g, ea);
 }
 
 template <int EPI>
 static hipError_t launch_gemm_epi(const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
                                   hipStream_t st) {
-  int waves = gemm_waves(g);
-  // the RoPE/KV-write and vocab epilogues need more than 128 registers per lane
-  if ((EPI == EPI_QKV || EPI == EPI_LOGITS) && waves > 8) waves = 8;
-  switch (waves) {
-    case 16:
-      if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU) launch_gemm_w<EPI, 16>(W, X, g, ea, st);
-      break;
-    case 8: launch_gemm_w<EPI, 8>(W, X, g, ea, st); break;
-    default: launch_gemm_w<EPI, 4>(W, X, g, ea, st); break;
-  }
+  if (g.WAVES == 8) launch_gemm_w<EPI, 8>(W, X, g, ea, st);
+  else launch_gemm_w<EPI, 4>(W, X, g, ea, st);
   return hipGetLastError();
 }
 
@@ -419,194 +475,250 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const
     case EPI_QKV: return launch_gemm_epi<EPI_QKV>(W, X, g, ea, st);
     case EPI_RESID: return launch_gemm_epi<EPI_RESID>(W, X, g, ea, st);
     case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(W, X, g, ea, st);
+    case EPI_PARTIAL: return launch_gemm_epi<EPI_PARTIAL>(W, X, g, ea, st);
     default: return launch_gemm_epi<EPI_LOGITS>(W, X, g, ea, st);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Block attention, bf16, head_dim 128, over the paged cache.
-// grid (splits, Hkv, slots), 4 waves.  Workgroup (sp, g, slot) covers the
-// absolute key range [sp*256, sp*256+256) of KV head g for every query column
-// (q head of the group, block row); wave w takes query tiles w, w+4, ...
-// S^T = K Q^T on MFMA (keys x query columns), an online softmax per column,
-// then O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts so the
-// product keeps ~16 bits of P.  Partials (O, max, sum) go to the workspace;
-// the combine kernel merges the splits in split order.  Masked keys add exact
-// zeros, so a row's result does not depend on how many rows the block has.
+// One workgroup per (256-key split, KV head g, 32-column query tile) of a
+// sequence slot; the query columns of KV head g are (q head of the group,
+// block row).  Wave w of the workgroup owns the 64 keys [j0 + 64w, j0 + 64w + 64)
+// -- exactly one KV page -- and loads that page's K and V blocks for head g
+// straight into registers (32 KiB, one burst).  Per 32-key tile: S^T = K Q^T
+// on MFMA (keys x query columns), an online softmax per column, then
+// O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts so the product
+// keeps ~16 bits of P.  The four waves' (max, sum, O) states are merged
+// through LDS in wave order and written as the split's partial; the combine
+// kernel merges splits in split order.  Masked keys contribute exact zeros and
+// every key range is an absolute range, so a row's result does not depend on
+// how many rows the block has.
+// Workgroups sharing a (split, head) pair get linear ids congruent mod 8 so
+// that they are placed on the same XCD and share its L2 for the K/V pages.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-  constexpr int kPagesPerSplit = kAttnSplitKeys / kPageTokens;
-  constexpr int kBlockVec = kPageTokens * kHd / 8;  // 16-byte vectors in one K (or V) page block
-  __shared__ u32x4 sK[kPagesPerSplit][kBlockVec];
-  __shared__ u32x4 sV[kPagesPerSplit][kBlockVec];
-  const int sp = blockIdx.x, g = blockIdx.y, slot = blockIdx.z;
+  __shared__ float s_ml[4][2][32];
+  __shared__ float s_o[4][kHd][32];
+  const int slot = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int seq = a.slots.ids[slot];
   const int T = a.slots.T;
   const int n = a.kv.seq_len[seq];
   const int nkeys = n + T;
-  const int j0 = sp * kAttnSplitKeys;
-  if (j0 >= nkeys) return;
-  const int j1 = min(j0 + kAttnSplitKeys, nkeys);
   const int Hkv = a.kv.Hkv;
   const int G = a.Hq / Hkv;
   const int nq = G * T;
   const int nqt = (nq + 31) >> 5;
-  const uint16_t* pool = (const uint16_t*)a.kv.pool;
-  const int* ptab = a.kv.page_table + (int64_t)seq * a.kv.max_pages;
-  const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
+  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  // linear id -> (pair = split * Hkv + g, query tile)
+  const int L = blockIdx.x;
+  const int qt = (L % (8 * nqt)) / 8;
+  const int pair = (L / (8 * nqt)) * 8 + (L % 8);
+  if (pair >= nsp * Hkv) return;
+  const int sp = pair / Hkv, g = pair % Hkv;
+  const int j0 = sp * kAttnSplitKeys;
+  const int jw = j0 + 64 * wave;  // this wave's page of keys
+  const bool wact = jw < nkeys;
+  const int jw1 = min(jw + 64, nkeys);
 
-  // stage this split's K and V page blocks in LDS: all loads issued before any store
-  const int npages = (j1 - j0 + kPageTokens - 1) / kPageTokens;
+  // K and V page blocks of head g for this wave's keys: 16 + 16 vectors per lane
+  u32x4 kv_k[16], kv_v[16];
+  if (wact) {
+    const int page = a.kv.page_table[(int64_t)seq * a.kv.max_pages + jw / kPageTokens];
+    const uint16_t* pb = (const uint16_t*)a.kv.pool + (int64_t)page * a.kv.page_elems + a.kv.layer_off;
+    const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
+    const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kv_k[i] = kb[i * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kv_v[i] = vb[i * 64 + lane];
+  }
+  const int c = qt * 32 + (lane & 31);
+  const bool cval = c < nq;
+  const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
+  const int head = g * G + hl;
+  const int qpos = n + t;
+  u32x4 qop[8];
   {
-    constexpr int kPer = kPagesPerSplit * kBlockVec / 256;  // vectors per thread per block kind
-    u32x4 bk[kPer], bv[kPer];
+    const u32x4* qp = (const u32x4*)(a.q + ((int64_t)(slot * T + t) * a.Hq + head) * kHd);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int p = idx / kBlockVec, o = idx % kBlockVec;
-      if (p < npages) {
-        const int64_t pb = (int64_t)ptab[j0 / kPageTokens + p] * a.kv.page_elems + a.kv.layer_off;
-        bk[i] = ((const u32x4*)(pool + pb + (int64_t)g * kPageTokens * kHd))[o];
-        bv[i] = ((const u32x4*)(pool + pb + (int64_t)(Hkv + g) * kPageTokens * kHd))[o];
-      }
+    for (int kb = 0; kb < 8; ++kb) qop[kb] = cval ? qp[2 * kb + h] : u32x4{0, 0, 0, 0};
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{0};
+
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int jt = jw + 32 * kt;
+    if (!wact || jt >= jw1) break;  // wave-uniform
+    f32x16 sacc = f32x16{0};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) sacc = mfma32(kv_k[kt * 8 + kb], qop[kb], sacc);
+    float sv[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = jt + crow(r, h);
+      const bool vis = cval && j < nkeys && (j < n || a.mode == BIDIR || j <= qpos);
+      sv[r] = vis ? sacc[r] * a.scale : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int p = idx / kBlockVec, o = idx % kBlockVec;
-      if (p < npages) {
-        sK[p][o] = bk[i];
-        sV[p][o] = bv[i];
+    for (int r = 0; r < 16; ++r) {
+      sv[r] = (sv[r] == -INFINITY) ? 0.f : __expf(sv[r] - m_new);
+      psum += sv[r];
+    }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+#pragma unroll
+    for (int ka = 0; ka < 2; ++ka) {
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = sv[8 * ka + e];
+        hi[e] = f2bf(p);
+        lo[e] = f2bf(p - bf2f(hi[e]));
+      }
+      u32x4 phi, plo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        phi[e] = (uint32_t)hi[2 * e] | ((uint32_t)hi[2 * e + 1] << 16);
+        plo[e] = (uint32_t)lo[2 * e] | ((uint32_t)lo[2 * e + 1] << 16);
+      }
+      const int kbv = 2 * kt + ka;  // 16-key group inside the page
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        o[dt] = mfma32(kv_v[dt * 4 + kbv], phi, o[dt]);
+        o[dt] = mfma32(kv_v[dt * 4 + kbv], plo, o[dt]);
       }
     }
   }
+  // merge the four waves' states (fixed wave order)
+  if (h == 0) {
+    s_ml[wave][0][lane & 31] = m_run;
+    s_ml[wave][1][lane & 31] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_o[wave][dt * 32 + crow(r, h)][lane & 31] = o[dt][r];
   __syncthreads();
-
-  for (int qt = wave; qt < nqt; qt += 4) {
-    const int c = qt * 32 + (lane & 31);
-    const bool cval = c < nq;
-    const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
-    const int head = g * G + hl;
-    const int qpos = n + t;
-    u32x4 qop[8];
-    {
-      const u32x4* qp = (const u32x4*)(a.q + ((int64_t)(slot * T + t) * a.Hq + head) * kHd);
+  const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
+  const int col = threadIdx.x & 31;
+  const int cc = qt * 32 + col;
+  if (cc < nq) {
+    float M = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) qop[kb] = cval ? qp[2 * kb + h] : u32x4{0, 0, 0, 0};
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][col]);
+    float wgt[4];
+    float Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_ml[w][0][col];
+      wgt[w] = (mw == -INFINITY) ? 0.f : __expf(mw - M);
+      Lsum += wgt[w] * s_ml[w][1][col];
     }
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 o[4];
+    float* op = a.opart + base_idx * kHd * a.nq_pad;
+    for (int d = threadIdx.x >> 5; d < kHd; d += 8) {
+      float v = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = f32x16{0};
-
-    for (int jt = j0; jt < j1; jt += 32) {
-      const int pi = (jt - j0) / kPageTokens;
-      const int kt = (jt % kPageTokens) >> 5;
-      f32x16 sacc = f32x16{0};
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) sacc = mfma32(sK[pi][(kt * 8 + kb) * 64 + lane], qop[kb], sacc);
-      float sv[16];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jt + crow(r, h);
-        const bool vis = cval && j < nkeys && (j < n || a.mode == BIDIR || j <= qpos);
-        sv[r] = vis ? sacc[r] * a.scale : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = (sv[r] == -INFINITY) ? 0.f : __expf(sv[r] - m_new);
-        psum += sv[r];
-      }
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-#pragma unroll
-      for (int ka = 0; ka < 2; ++ka) {
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = sv[8 * ka + e];
-          hi[e] = f2bf(p);
-          lo[e] = f2bf(p - bf2f(hi[e]));
-        }
-        u32x4 phi, plo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          phi[e] = (uint32_t)hi[2 * e] | ((uint32_t)hi[2 * e + 1] << 16);
-          plo[e] = (uint32_t)lo[2 * e] | ((uint32_t)lo[2 * e + 1] << 16);
-        }
-        const int kbv = ((jt % kPageTokens) >> 4) + ka;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const u32x4 vop = sV[pi][(dt * (kPageTokens / 16) + kbv) * 64 + lane];
-          o[dt] = mfma32(vop, phi, o[dt]);
-          o[dt] = mfma32(vop, plo, o[dt]);
-        }
-      }
+      for (int w = 0; w < 4; ++w) v += wgt[w] * s_o[w][d][col];
+      op[(int64_t)d * a.nq_pad + cc] = v;
     }
-    if (cval) {
-      float* op = a.opart + base_idx * kHd * a.nq_pad;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) op[(int64_t)(dt * 32 + crow(r, h)) * a.nq_pad + c] = o[dt][r];
-      if (h == 0) {
-        a.mlpart[(base_idx * 2 + 0) * a.nq_pad + c] = m_run;
-        a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = l_run;
-      }
+    if (threadIdx.x < 32) {
+      a.mlpart[(base_idx * 2 + 0) * a.nq_pad + cc] = M;
+      a.mlpart[(base_idx * 2 + 1) * a.nq_pad + cc] = Lsum;
     }
   }
 }
 
-// o = sum_s w_s O_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s); rounded to bf16.
+// Merge the splits for 32 query columns x 16 dims of one (slot, KV head):
+// o = sum_s w_s O_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s), split
+// order fixed; rounded to bf16.  The splits' (m, l) go to LDS with all 256
+// threads loading, the weights are formed there, then every thread sums two
+// (dim, column) outputs with its partial-O loads issued 8 splits at a time.
+constexpr int kMaxSplits = 256;  // 65536 keys
+
 __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
-  const int g = blockIdx.y, slot = blockIdx.z;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int c = idx % a.nq_pad, d = idx / a.nq_pad;
+  __shared__ float s_m[kMaxSplits][32];
+  __shared__ float s_l[kMaxSplits][32];
+  __shared__ float s_inv[32];
+  const int ct = blockIdx.x, dch = blockIdx.y % (kHd / 16), g = blockIdx.y / (kHd / 16), slot = blockIdx.z;
   const int T = a.slots.T;
   const int Hkv = a.kv.Hkv, G = a.Hq / Hkv, nq = G * T;
-  if (d >= kHd || c >= nq) return;
   const int seq = a.slots.ids[slot];
   const int nkeys = a.kv.seq_len[seq] + T;
   const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
   const int64_t b0 = ((int64_t)slot * Hkv + g) * a.max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.mlpart[((b0 + s) * 2) * a.nq_pad + c]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float ms = a.mlpart[((b0 + s) * 2) * a.nq_pad + c];
-    if (ms == -INFINITY) continue;
-    const float w = __expf(ms - M);
-    L += w * a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c];
-    acc += w * a.opart[((b0 + s) * kHd + d) * a.nq_pad + c];
+  const int col = threadIdx.x & 31, row = threadIdx.x >> 5;
+  const int c = ct * 32 + col;
+  const bool cval = c < nq;
+  for (int s = row; s < nsp; s += 8) {
+    s_m[s][col] = cval ? a.mlpart[((b0 + s) * 2) * a.nq_pad + c] : -INFINITY;
+    s_l[s][col] = cval ? a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c] : 0.f;
   }
-  const float o = acc / L;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, s_m[s][col]);
+    float L = 0.f;
+    for (int s = 0; s < nsp; ++s) {
+      const float ms = s_m[s][col];
+      const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+      s_m[s][col] = w;  // weight replaces the max
+      L += w * s_l[s][col];
+    }
+    s_inv[col] = 1.f / L;
+  }
+  __syncthreads();
+  if (!cval) return;
   const int hl = c / T, t = c % T;
   const int64_t m = (int64_t)slot * T + t;
-  const int64_t k = (int64_t)(g * G + hl) * kHd + d;
   const int64_t K = (int64_t)a.Hq * kHd;
-  if (a.out_packed) a.out[packed_index(m, k, K)] = f2bf(o);
-  else a.out[m * K + k] = f2bf(o);
+  const float inv = s_inv[col];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int d = dch * 16 + row + 8 * j;
+    const float* op = a.opart + (b0 * kHd + d) * a.nq_pad + c;
+    float acc = 0.f;
+    int s = 0;
+    for (; s + 8 <= nsp; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = op[(int64_t)(s + i) * kHd * a.nq_pad];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += s_m[s + i][col] * v[i];
+    }
+    for (; s < nsp; ++s) acc += s_m[s][col] * op[(int64_t)s * kHd * a.nq_pad];
+    const float o = acc * inv;
+    const int64_t k = (int64_t)(g * G + hl) * kHd + d;
+    if (a.out_packed) a.out[packed_index(m, k, K)] = f2bf(o);
+    else a.out[m * K + k] = f2bf(o);
+  }
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_bf16, dim3(grid_splits, a.kv.Hkv, a.slots.n_seq), dim3(256), 0, st, a);
+  const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
+  const int pairs = grid_splits * a.kv.Hkv;
+  const int grid = (pairs + 7) / 8 * 8 * nqt;
+  hipLaunchKernelGGL(k_attn_bf16, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {
-  const int n = a.nq_pad * kHd;
-  hipLaunchKernelGGL(k_attn_combine_bf16, dim3((n + 255) / 256, a.kv.Hkv, a.slots.n_seq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_attn_combine_bf16, dim3(a.nq_pad / 32, a.kv.Hkv * (kHd / 16), a.slots.n_seq), dim3(256), 0, st,
+                     a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ sdm_status check_config(const sdm_config* c) {
   if (c->max_seqs < 1 || c->max_block < 1 || c->max_context < 2 || c->max_rows < 1)
     return fail(SDM_ERR_ARG, "non-positive capacity");
   if (c->max_block > c->max_rows) return fail(SDM_ERR_ARG, "max_block exceeds max_rows");
+  if (c->max_context > 65536) return fail(SDM_ERR_UNSUPPORTED, "max_context above 65536");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(SDM_ERR_ARG, "bad rms_eps or rope_base");
   if (c->dtype == SDM_BF16) {
     if (c->head_dim != kHd) return fail(SDM_ERR_UNSUPPORTED, "bf16 models need head_dim %d", kHd);
@@ -81,17 +82,9 @@ Dims dims_of(const sdm_config* c) {
   return D;
 }
 
-GemmShape gemm_shape(int N, int K, int rows) {
-  GemmShape g;
-  g.NT = N / 32;
-  g.KB = K / 16;
-  g.MTILES = (rows + 31) / 32;
-  return g;
-}
-
 struct Layout {
-  int64_t x, xn, q, attn, hbuf, ybuf, opart, mlpart, records, tok, conf, margin, rope_cos, rope_sin, page_table,
-      seq_len, total;
+  int64_t x, xn, q, attn, hbuf, ybuf, part, opart, mlpart, records, tok, conf, margin, rope_cos, rope_sin,
+      page_table, seq_len, total;
 };
 
 Layout layout_of(const sdm_config* c) {
@@ -112,6 +105,11 @@ Layout layout_of(const sdm_config* c) {
   int64_t ycols = 0;
   if (!D.bf16) ycols = std::max<int64_t>(std::max<int64_t>(D.qkv, 2LL * D.F), std::max<int64_t>(D.V, D.d));
   Lo.ybuf = take((int64_t)D.R * ycols * 4);
+  // split-K partials of the residual-stream projections (O and down)
+  int smax = 1;
+  if (D.bf16)
+    smax = std::max(gemm_config(EPI_PARTIAL, D.d, D.qd, D.R).S, gemm_config(EPI_PARTIAL, D.d, D.F, D.R).S);
+  Lo.part = take(D.bf16 ? (int64_t)smax * D.R * D.d * 4 : 0);
   Lo.opart = take(D.bf16 ? (int64_t)D.Hkv * D.max_splits * D.hd * D.nq_cap * 4 : 0);
   Lo.mlpart = take(D.bf16 ? (int64_t)D.Hkv * D.max_splits * 2 * D.nq_cap * 4 : 0);
   const int n_vtiles = (D.V + 31) / 32;
@@ -279,15 +277,22 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   ea.n_vtiles = (D.V + 31) / 32;
   ea.V = D.V;
   ea.mask_id = m->cfg.mask_id;
+  ea.part = m->at<float>(m->lo.part);
+  ea.part_stride = (int64_t)D.R * D.d;
   const float eps = m->cfg.rms_eps;
+  int nparts = 0;  // split-K partials waiting to be added to the residual by the next RMSNorm
 
   for (int l = 0; l < D.L; ++l) {
     ea.kv = kv_view(m, l);
     { TimedScope ts(m, SDM_K_NORM);
-      HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, m->attn_norm[l], eps, M, D.d, 0, xn, st), "rmsnorm"); }
+      HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->attn_norm[l], eps, M, D.d, 0, xn,
+                             st),
+              "rmsnorm"); }
+    nparts = 0;
     if (D.bf16) {
       { TimedScope ts(m, SDM_K_QKV);
-      HIP_TRY(launch_gemm_bf16(EPI_QKV, (const uint16_t*)m->w_qkv[l], (const uint16_t*)xn, gemm_shape(D.qkv, D.d, M),
+      HIP_TRY(launch_gemm_bf16(EPI_QKV, (const uint16_t*)m->w_qkv[l], (const uint16_t*)xn,
+                               gemm_config(EPI_QKV, D.qkv, D.d, M),
                                ea, st),
               "qkv gemm"); }
       AttnArgs aa{};
@@ -311,16 +316,23 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       { TimedScope ts(m, SDM_K_ATTN_COMBINE);
         HIP_TRY(launch_attn_combine_bf16(aa, st), "attention combine"); }
       { TimedScope ts(m, SDM_K_O);
-        HIP_TRY(launch_gemm_bf16(EPI_RESID, (const uint16_t*)m->w_o[l], aa.out, gemm_shape(D.d, D.qd, M), ea, st),
+        const GemmShape go = gemm_config(EPI_PARTIAL, D.d, D.qd, M);
+        nparts = go.S;
+        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_o[l], aa.out, go, ea, st),
                 "o gemm"); }
       { TimedScope ts(m, SDM_K_NORM);
-        HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, m->ffn_norm[l], eps, M, D.d, 0, xn, st), "rmsnorm"); }
+        HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->ffn_norm[l], eps, M, D.d, 0, xn,
+                               st),
+                "rmsnorm"); }
+      nparts = 0;
       { TimedScope ts(m, SDM_K_GATE_UP);
         HIP_TRY(launch_gemm_bf16(EPI_SWIGLU, (const uint16_t*)m->w_gu[l], (const uint16_t*)xn,
-                                 gemm_shape(2 * D.F, D.d, M), ea, st),
+                                 gemm_config(EPI_SWIGLU, 2 * D.F, D.d, M), ea, st),
                 "gate/up gemm"); }
       { TimedScope ts(m, SDM_K_DOWN);
-        HIP_TRY(launch_gemm_bf16(EPI_RESID, (const uint16_t*)m->w_down[l], ea.h_out, gemm_shape(D.d, D.F, M), ea, st),
+        const GemmShape gd = gemm_config(EPI_PARTIAL, D.d, D.F, M);
+        nparts = gd.S;
+        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_down[l], ea.h_out, gd, ea, st),
                 "down gemm"); }
     } else {
       float* y = m->at<float>(m->lo.ybuf);
@@ -333,7 +345,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       HIP_TRY(launch_attention_f32(qf, ea.kv, sl, D.Hq, mode, af, st), "attention");
       HIP_TRY(launch_gemm_f32(af, (const float*)m->w_o[l], M, D.d, D.qd, y, st), "o gemm");
       HIP_TRY(launch_resid_f32(y, x, M, D.d, st), "residual");
-      HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, m->ffn_norm[l], eps, M, D.d, 0, xn, st), "rmsnorm");
+      HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, nullptr, 0, 0, m->ffn_norm[l], eps, M, D.d, 0, xn, st), "rmsnorm");
       HIP_TRY(launch_gemm_f32((const float*)xn, (const float*)m->w_gu[l], M, 2 * D.F, D.d, y, st), "gate/up gemm");
       HIP_TRY(launch_swiglu_f32(y, hf, M, D.F, st), "swiglu");
       HIP_TRY(launch_gemm_f32(hf, (const float*)m->w_down[l], M, D.d, D.F, y, st), "down gemm");
@@ -343,12 +355,14 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   // final norm + LM head on the rows whose logits are needed
   const int ML = logits_last_only ? 1 : M;
   const int row0 = logits_last_only ? M - 1 : 0;
-  HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, m->final_norm, eps, ML, D.d, row0, xn, st), "final rmsnorm");
+  HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->final_norm, eps, ML, D.d, row0, xn, st),
+          "final rmsnorm");
   ea.M = ML;
   ea.logits = d_logits;
   if (D.bf16) {
     TimedScope ts(m, SDM_K_LM_HEAD);
-    HIP_TRY(launch_gemm_bf16(EPI_LOGITS, (const uint16_t*)m->lm_head, (const uint16_t*)xn, gemm_shape(D.V, D.d, ML),
+    HIP_TRY(launch_gemm_bf16(EPI_LOGITS, (const uint16_t*)m->lm_head, (const uint16_t*)xn,
+                             gemm_config(EPI_LOGITS, D.V, D.d, ML),
                              ea, st),
             "lm head");
   } else {
@@ -785,6 +799,7 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
   if (head_dim != kHd) return fail(SDM_ERR_UNSUPPORTED, "attention op needs head_dim %d", kHd);
   if (!d_q || !d_pool || !d_pages || !d_out || !d_workspace) return fail(SDM_ERR_ARG, "null pointer");
   if (n_prefix < 0 || T < 1 || T > 4096) return fail(SDM_ERR_ARG, "bad n_prefix / T");
+  if ((int64_t)n_prefix + T > 65536) return fail(SDM_ERR_UNSUPPORTED, "more than 65536 keys");
   if (mode != SDM_CAUSAL && mode != SDM_BIDIR) return fail(SDM_ERR_ARG, "bad mode");
   int64_t off_ml, off_len;
   const int64_t need = attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml, &off_len);
