@@ -52,6 +52,24 @@ def kernel_bytes(s, cls: str, M: int) -> int:
     return lw[cls] + io[cls]
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_gemm_8b_selfspec_hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "self_speculative_amd", "csrc", "sdm_kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    --pmc record, or None if the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_RECORD) if "=" in l and not l.startswith("#"))
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256") != sha:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +79,8 @@ def main() -> int:
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline pass only (for profilers)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not part of it "
@@ -174,7 +194,8 @@ def main() -> int:
         achieved = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
         out["roofline"] = {"bound": "hbm", "kernel": "k_gemm_bf16<EPI_SWIGLU> (gate/up + SwiGLU), M=32",
                            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                            "bytes_per_launch": gu_bytes, "avg_launch_us": gu["avg_us"]}
         # whole forward vs roofline
         f_us = per["forward"]["avg_us"]
@@ -223,6 +244,16 @@ def main() -> int:
                                             "tpf": round(tokens / (2 * K), 3)},
                         "prefill_1024_ms": round(t_pf * 1e3, 2)}
 
+    if args.calib_copy:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(s, weights, prompt, tokens / K, log)
     model.close()

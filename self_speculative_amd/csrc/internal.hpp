@@ -1,6 +1,7 @@
 // Internal declarations shared by the host runtime (sdm_runtime.cpp) and the
 // gfx950 kernels (sdm_kernels.hip).  Not part of the public C ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -139,6 +140,25 @@ struct FinishArgs {
   float tau; int force_all;
   int* next;             // NEXT: device token (last row of slot 0)
 };
+
+// Kernel timing: when set, the next launch carries these events on its own
+// dispatch (start / completion), then the slot is cleared.
+struct KernelTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local KernelTiming g_ktiming;
+
+// Launch a kernel, attaching g_ktiming's events to this dispatch when set.
+#define SDM_LAUNCH(kern, grid, block, shmem, stream, ...)                                                        \
+  do {                                                                                                          \
+    if (::sdm::g_ktiming.start) {                                                                               \
+      hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, ::sdm::g_ktiming.start, ::sdm::g_ktiming.stop, 0, \
+                            __VA_ARGS__);                                                                       \
+      ::sdm::g_ktiming = ::sdm::KernelTiming{};                                                                 \
+    } else {                                                                                                    \
+      hipLaunchKernelGGL(kern, grid, block, shmem, stream, __VA_ARGS__);                                        \
+    }                                                                                                           \
+  } while (0)
 
 // ---- launchers (sdm_kernels.hip) -------------------------------------------
 hipError_t launch_pack(int dtype, int kind, const void* src, const void* src2, void* dst, int64_t rows, int64_t cols,

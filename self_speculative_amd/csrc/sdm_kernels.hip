@@ -24,6 +24,8 @@
 
 namespace sdm {
 
+thread_local KernelTiming g_ktiming;
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -76,14 +78,14 @@ hipError_t launch_pack(int dtype, int kind, const void* src, const void* src2, v
   const int64_t n = rows * cols;
   const dim3 blk(256), grd((unsigned)((n + 255) / 256));
   if (dtype == 1) {
-    hipLaunchKernelGGL(k_pack_bf16, grd, blk, 0, st, kind, (const uint16_t*)src, 0, (uint16_t*)dst, rows, cols, cols,
+    SDM_LAUNCH(k_pack_bf16, grd, blk, 0, st, kind, (const uint16_t*)src, 0, (uint16_t*)dst, rows, cols, cols,
                        head_dim);
     if (kind == 2)
-      hipLaunchKernelGGL(k_pack_bf16, grd, blk, 0, st, kind, (const uint16_t*)src2, 1, (uint16_t*)dst, rows, cols,
+      SDM_LAUNCH(k_pack_bf16, grd, blk, 0, st, kind, (const uint16_t*)src2, 1, (uint16_t*)dst, rows, cols,
                          cols, head_dim);
   } else {
-    hipLaunchKernelGGL(k_copy_f32, grd, blk, 0, st, (const float*)src, (float*)dst, n);
-    if (kind == 2) hipLaunchKernelGGL(k_copy_f32, grd, blk, 0, st, (const float*)src2, (float*)dst + n, n);
+    SDM_LAUNCH(k_copy_f32, grd, blk, 0, st, (const float*)src, (float*)dst, n);
+    if (kind == 2) SDM_LAUNCH(k_copy_f32, grd, blk, 0, st, (const float*)src2, (float*)dst + n, n);
   }
   return hipGetLastError();
 }
@@ -112,10 +114,10 @@ __global__ void k_embed(const T* __restrict__ E, int d, int V, const int* __rest
 hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* tokens, int tok_src, const int* anchor,
                         int M, int T, int mask_id, float* x, hipStream_t st) {
   if (dtype == 1)
-    hipLaunchKernelGGL(k_embed<uint16_t>, dim3(M), dim3(256), 0, st, (const uint16_t*)E, d, V, tokens, tok_src,
+    SDM_LAUNCH(k_embed<uint16_t>, dim3(M), dim3(256), 0, st, (const uint16_t*)E, d, V, tokens, tok_src,
                        anchor, T, mask_id, x);
   else
-    hipLaunchKernelGGL(k_embed<float>, dim3(M), dim3(256), 0, st, (const float*)E, d, V, tokens, tok_src, anchor, T,
+    SDM_LAUNCH(k_embed<float>, dim3(M), dim3(256), 0, st, (const float*)E, d, V, tokens, tok_src, anchor, T,
                        mask_id, x);
   return hipGetLastError();
 }
@@ -206,10 +208,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ x
 hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
                           float eps, int M, int d, int row0, void* out, hipStream_t st) {
   if (dtype == 1)
-    hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, part, nparts, part_stride,
+    SDM_LAUNCH(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, part, nparts, part_stride,
                        (const uint16_t*)gain, eps, d, row0, (uint16_t*)out);
   else
-    hipLaunchKernelGGL(k_rmsnorm_f32, dim3(M), dim3(256), 0, st, x, (const float*)gain, eps, d, row0, (float*)out);
+    SDM_LAUNCH(k_rmsnorm_f32, dim3(M), dim3(256), 0, st, x, (const float*)gain, eps, d, row0, (float*)out);
   return hipGetLastError();
 }
 
@@ -456,9 +458,9 @@ static void launch_gemm_w(const uint16_t* W, const uint16_t* X, const GemmShape&
   const dim3 grd(g.NT, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
   // split-K partial GEMMs stream with 8-deep batches (more waves resident per SIMD)
   constexpr int U1 = EPI == EPI_PARTIAL ? 8 : 16;
-  if (MT == 1) hipLaunchKernelGGL((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, g, ea);
-  else if (MT == 2) hipLaunchKernelGGL((k_gemm_bf16<EPI, 2, 8, WAVES>), grd, blk, 0, st, W, X, g, ea);
-  else hipLaunchKernelGGL((k_gemm_bf16<EPI, 4, 4, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  if (MT == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  else if (MT == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 8, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  else SDM_LAUNCH((k_gemm_bf16<EPI, 4, 4, WAVES>), grd, blk, 0, st, W, X, g, ea);
 }
 
 template <int EPI>
@@ -713,11 +715,11 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
   const int pairs = grid_splits * a.kv.Hkv;
   const int grid = (pairs + 7) / 8 * 8 * nqt;
-  hipLaunchKernelGGL(k_attn_bf16, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
+  SDM_LAUNCH(k_attn_bf16, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_combine_bf16, dim3(a.nq_pad / 32, a.kv.Hkv * (kHd / 16), a.slots.n_seq), dim3(256), 0, st,
+  SDM_LAUNCH(k_attn_combine_bf16, dim3(a.nq_pad / 32, a.kv.Hkv * (kHd / 16), a.slots.n_seq), dim3(256), 0, st,
                      a);
   return hipGetLastError();
 }
@@ -737,7 +739,7 @@ __global__ void k_attn_pack_kv(int Hkv, const uint16_t* __restrict__ k, const ui
 hipError_t launch_attn_pack_kv(int Hkv, const uint16_t* k, const uint16_t* v, int n_keys, const int* pages,
                                uint16_t* pool, hipStream_t st) {
   const int64_t n = (int64_t)n_keys * Hkv * kHd;
-  hipLaunchKernelGGL(k_attn_pack_kv, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Hkv, k, v, n_keys, pages,
+  SDM_LAUNCH(k_attn_pack_kv, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Hkv, k, v, n_keys, pages,
                      pool);
   return hipGetLastError();
 }
@@ -813,8 +815,8 @@ __global__ void k_finish_mode(FinishArgs f) {
 }
 
 hipError_t launch_finish(const FinishArgs& f, hipStream_t st) {
-  hipLaunchKernelGGL(k_select_rows, dim3(f.M), dim3(256), 0, st, f.records, f.n_vtiles, f.tok, f.conf, f.margin);
-  hipLaunchKernelGGL(k_finish_mode, dim3(f.slots.n_seq), dim3(64), 0, st, f);
+  SDM_LAUNCH(k_select_rows, dim3(f.M), dim3(256), 0, st, f.records, f.n_vtiles, f.tok, f.conf, f.margin);
+  SDM_LAUNCH(k_finish_mode, dim3(f.slots.n_seq), dim3(64), 0, st, f);
   return hipGetLastError();
 }
 
@@ -833,7 +835,7 @@ __global__ void k_gemm_f32(const float* __restrict__ X, const float* __restrict_
   Y[(int64_t)m * N + n] = acc;
 }
 hipError_t launch_gemm_f32(const float* X, const float* W, int M, int N, int K, float* Y, hipStream_t st) {
-  hipLaunchKernelGGL(k_gemm_f32, dim3((N + 127) / 128, M), dim3(128), 0, st, X, W, M, N, K, Y);
+  SDM_LAUNCH(k_gemm_f32, dim3((N + 127) / 128, M), dim3(128), 0, st, X, W, M, N, K, Y);
   return hipGetLastError();
 }
 
@@ -872,7 +874,7 @@ __global__ void k_qkv_post_f32(const float* __restrict__ Y, EpiArgs ea, int hd) 
   }
 }
 hipError_t launch_qkv_post_f32(const float* Y, const EpiArgs& ea, int hd, hipStream_t st) {
-  hipLaunchKernelGGL(k_qkv_post_f32, dim3(ea.M), dim3(128), 0, st, Y, ea, hd);
+  SDM_LAUNCH(k_qkv_post_f32, dim3(ea.M), dim3(128), 0, st, Y, ea, hd);
   return hipGetLastError();
 }
 
@@ -918,7 +920,7 @@ __global__ void k_attn_f32(const float* __restrict__ q, KvView kv, Slots sl, int
 }
 hipError_t launch_attention_f32(const float* q, const KvView& kv, const Slots& sl, int Hq, int mode, float* out,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_f32, dim3(sl.n_seq * sl.T), dim3(64), 0, st, q, kv, sl, Hq, mode, out);
+  SDM_LAUNCH(k_attn_f32, dim3(sl.n_seq * sl.T), dim3(64), 0, st, q, kv, sl, Hq, mode, out);
   return hipGetLastError();
 }
 
@@ -928,7 +930,7 @@ __global__ void k_resid_f32(const float* __restrict__ Y, float* __restrict__ x, 
 }
 hipError_t launch_resid_f32(const float* Y, float* x, int M, int d, hipStream_t st) {
   const int64_t n = (int64_t)M * d;
-  hipLaunchKernelGGL(k_resid_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Y, x, n);
+  SDM_LAUNCH(k_resid_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Y, x, n);
   return hipGetLastError();
 }
 
@@ -941,7 +943,7 @@ __global__ void k_swiglu_f32(const float* __restrict__ Y, float* __restrict__ ho
 }
 hipError_t launch_swiglu_f32(const float* Y, float* h, int M, int F, hipStream_t st) {
   const int64_t n = (int64_t)M * F;
-  hipLaunchKernelGGL(k_swiglu_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Y, h, M, F);
+  SDM_LAUNCH(k_swiglu_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Y, h, M, F);
   return hipGetLastError();
 }
 
@@ -960,7 +962,7 @@ __global__ void k_logit_records_f32(const float* __restrict__ Y, EpiArgs ea) {
   ea.records[(int64_t)m * ea.n_vtiles + vt] = rec_pack(a);
 }
 hipError_t launch_logit_records_f32(const float* Y, const EpiArgs& ea, hipStream_t st) {
-  hipLaunchKernelGGL(k_logit_records_f32, dim3((ea.n_vtiles + 63) / 64, ea.M), dim3(64), 0, st, Y, ea);
+  SDM_LAUNCH(k_logit_records_f32, dim3((ea.n_vtiles + 63) / 64, ea.M), dim3(64), 0, st, Y, ea);
   return hipGetLastError();
 }
 
@@ -976,7 +978,7 @@ __global__ void k_set_ints(int* dst, IntVals vals, int n) {
 hipError_t launch_set_ints(int* dst, const int* vals, int n, hipStream_t st) {
   IntVals iv;
   for (int i = 0; i < n && i < 64; ++i) iv.v[i] = vals[i];
-  hipLaunchKernelGGL(k_set_ints, dim3(1), dim3(64), 0, st, dst, iv, n);
+  SDM_LAUNCH(k_set_ints, dim3(1), dim3(64), 0, st, dst, iv, n);
   return hipGetLastError();
 }
 

@@ -210,15 +210,27 @@ sdm_status set_len(sdm_model* m, int32_t seq, int32_t len) {
   return SDM_OK;
 }
 
-// Event pair around launches of the timed kernel class (no-op otherwise).
+// Timing of the launches of one kernel class: the events ride on the kernel's
+// own dispatch (start / completion).  A whole forward is bracketed by a pair of
+// stream events instead.
 struct TimedScope {
   sdm_model* m;
   bool on;
-  TimedScope(sdm_model* mm, int cls) : m(mm), on(mm->timed_class == cls && mm->ev_used < mm->ev_begin.size()) {
-    if (on) hipEventRecord(m->ev_begin[m->ev_used], m->stream);
+  int cls;
+  TimedScope(sdm_model* mm, int c) : m(mm), on(mm->timed_class == c && mm->ev_used < mm->ev_begin.size()), cls(c) {
+    if (!on) return;
+    if (cls == SDM_K_FORWARD) {
+      hipEventRecord(m->ev_begin[m->ev_used], m->stream);
+    } else {
+      g_ktiming.start = m->ev_begin[m->ev_used];
+      g_ktiming.stop = m->ev_end[m->ev_used];
+    }
   }
   ~TimedScope() {
-    if (on) hipEventRecord(m->ev_end[m->ev_used++], m->stream);
+    if (!on) return;
+    if (cls == SDM_K_FORWARD) hipEventRecord(m->ev_end[m->ev_used], m->stream);
+    g_ktiming = KernelTiming{};
+    ++m->ev_used;
   }
 };
 
