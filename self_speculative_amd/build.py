@@ -30,6 +30,10 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU ops are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # no implicit multiply-add fusion: each template instantiation of an
+           # epilogue (one per activation-tile count) then rounds identically,
+           # so a row's result does not depend on the batch it is computed in
+           "-ffp-contract=off",
            "-I", os.path.join(ROOT, "include"),
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
     if verbose:
