@@ -20,14 +20,14 @@ The forward, written out (pre-norm decoder, no biases, untied LM head):
 
     h      = E[x]                                   residual stream, float
     for each layer:
-      a    = R(rms(h) * g1)
-      q    = R(rope(a Wq^T, p)),  k = R(rope(a Wk^T, p)),  v = R(a Wv^T)
+      a    = A(rms(h) * g1)
+      q    = A(rope(a Wq^T, p)),  k = R(rope(a Wk^T, p)),  v = R(a Wv^T)
       o    = softmax over visible keys of (q . k / sqrt(hd)) applied to v
-      h    = h + R(o) Wo^T
-      b    = R(rms(h) * g2)
-      u    = R(silu(b Wg^T) * (b Wu^T))
+      h    = h + A(o) Wo^T
+      b    = A(rms(h) * g2)
+      u    = A(silu(b Wg^T) * (b Wu^T))
       h    = h + u Wd^T
-    logits = R(rms(h) * gf) Wlm^T
+    logits = A(rms(h) * gf) Wlm^T
 
 with rms(h) = h / sqrt(mean(h^2) + eps), silu(x) = x / (1 + exp(-x)), key j
 visible to block row i (absolute positions, block starts at n) iff j < n, or
@@ -35,11 +35,14 @@ j is in the block and (bidirectional, or j <= n + i); query head h uses KV
 head floor(h * Hkv / Hq); rope rotates the pairs (t, t + hd/2) by the angle
 p * base^(-2t/hd), the angle taken in float64 and cos/sin rounded to float32.
 
-R() is the rounding to bf16 (nearest, ties to even) applied at every tensor the
-bf16 model keeps in bf16 storage: weights, the normalised activations, q/k/v
-after RoPE (hence the KV cache), the attention output and the SwiGLU product.
-The residual stream and the logits stay wide.  For float32 shapes R() is the
-identity.  Arithmetic between rounding points is float64 by default.
+Storage precision of a bf16 shape.  R() is the rounding to bf16 (nearest,
+ties to even): the weights and k/v after RoPE -- the paged KV cache -- are
+bf16.  A() is the rounding of an activation that one kernel hands to the next
+(the normalised activations, q, the attention output, the SwiGLU product) to a
+two-term bf16 expansion, hi = R(x), lo = R(x - hi), value hi + lo: about 16
+significant bits, which the bf16 matrix units consume as two products.  The
+residual stream and the logits stay wide.  For float32 shapes R() and A() are
+the identity.  Arithmetic between rounding points is float64 by default.
 
 Row selection on a logits row (MASK excluded everywhere): tok = smallest id
 reaching the max, conf = 1 / sum_v exp(l_v - max), margin = max minus the
@@ -82,6 +85,15 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     with np.errstate(invalid="ignore"):
         r = np.rint(x / q) * q                          # rint: half to even
     return np.where(x == 0, x, r)
+
+
+def bf16_pair_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to a two-term bf16 expansion: hi = bf16(x), lo = bf16(x - hi),
+    returned as the float64 value hi + lo (exact: both terms are bf16 numbers
+    within 2^-8 of each other's scale)."""
+    x = np.asarray(x, dtype=np.float64)
+    hi = bf16_round(x)
+    return hi + bf16_round(x - hi)
 
 
 def decode_bf16_bits(b: np.ndarray) -> np.ndarray:
@@ -232,7 +244,12 @@ class OracleModel:
         return np.asarray(a).astype(self.dtype)
 
     def R(self, x: np.ndarray) -> np.ndarray:
+        """bf16 storage (the KV cache)."""
         return bf16_round(x).astype(self.dtype, copy=False) if self.bf16 else x
+
+    def A(self, x: np.ndarray) -> np.ndarray:
+        """Two-term bf16 storage of an activation handed between kernels."""
+        return bf16_pair_round(x).astype(self.dtype, copy=False) if self.bf16 else x
 
     def layer(self, l: int) -> LayerWeights:
         if l in self._layers:
@@ -293,20 +310,20 @@ class OracleModel:
         h = self.embed_rows(tokens)
         for l in range(s.n_layers):
             w = self.layer(l)
-            a = self.R(self._norm(h, w.attn_norm))
-            q = self.R(apply_rope(self._mm(a, w.wq).reshape(T, s.n_q_heads, s.head_dim), cos, sin))
+            a = self.A(self._norm(h, w.attn_norm))
+            q = self.A(apply_rope(self._mm(a, w.wq).reshape(T, s.n_q_heads, s.head_dim), cos, sin))
             k = self.R(apply_rope(self._mm(a, w.wk).reshape(T, s.n_kv_heads, s.head_dim), cos, sin))
             v = self.R(self._mm(a, w.wv).reshape(T, s.n_kv_heads, s.head_dim))
             cache.K[l][n:n + T] = k
             cache.V[l][n:n + T] = v
             o = attention(q, cache.K[l][: n + T], cache.V[l][: n + T], n, mode, self.row_independent)
-            h = h + self._mm(self.R(o.reshape(T, s.q_dim)), w.wo)
-            b = self.R(self._norm(h, w.ffn_norm))
-            u = self.R(silu(self._mm(b, w.wg)) * self._mm(b, w.wu))
+            h = h + self._mm(self.A(o.reshape(T, s.q_dim)), w.wo)
+            b = self.A(self._norm(h, w.ffn_norm))
+            u = self.A(silu(self._mm(b, w.wg)) * self._mm(b, w.wu))
             h = h + self._mm(u, w.wd)
         if logits_rows is not None:
             h = h[np.asarray(logits_rows)]
-        z = self.R(self._norm(h, self.final_norm))
+        z = self.A(self._norm(h, self.final_norm))
         return self._mm(z, self.lm_head())
 
     def new_cache(self, capacity: int = 64) -> KVCache:

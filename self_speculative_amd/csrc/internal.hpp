@@ -18,6 +18,12 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTI
 enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3 };
 enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1 };
 
+// Activations of the bf16 path travel between kernels as two bf16 planes, hi
+// and lo, with value hi + lo: hi = RNE_bf16(x), lo = RNE_bf16(x - hi) (a
+// two-term bf16 expansion, about 16 significant bits).  Every plane pair is
+// one buffer with the lo plane `plane` elements after the hi plane.  Weights
+// and the KV cache are single bf16 values.
+
 // Element (r, c) of a [R, C] matrix in the MFMA 32x32x16 operand layout:
 // tiles of 32 rows x 16 columns, 1 KiB each, laid out row-tile major; inside
 // a tile lane = (r % 32) + 32 * ((c % 16) / 8) holds the 8 columns c%8.
@@ -69,12 +75,14 @@ struct EpiArgs {
   Slots slots;
   KvView kv;
   int Hq;
-  uint16_t* q_out;       // QKV: [M][Hq][hd]
+  uint16_t* q_out;       // QKV: [M][Hq][hd] hi plane, lo plane q_plane elements later
+  int64_t q_plane;
   const float* rope_cos; // [max_context][hd/2]
   const float* rope_sin;
   float* x;              // RESID: residual [M][d]
   int d;
-  uint16_t* h_out;       // SWIGLU: packed-B [M32][F]
+  uint16_t* h_out;       // SWIGLU: packed-B [M32][F] hi plane, lo plane h_plane elements later
+  int64_t h_plane;
   int F;
   float4* records;       // LOGITS: [M][n_vtiles] (max, idx bits, max2, sum)
   int n_vtiles;
@@ -112,7 +120,8 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
 }
 
 struct AttnArgs {
-  const uint16_t* q;     // [rows][Hq][hd] (row-major)
+  const uint16_t* q;     // [rows][Hq][hd] (row-major) hi plane
+  int64_t q_plane;       // elements to the lo plane; 0: q is plain bf16
   KvView kv;
   Slots slots;
   int Hq, mode;
@@ -122,6 +131,7 @@ struct AttnArgs {
   int max_splits, nq_pad;
   uint16_t* out;         // [rows][Hq*hd]: packed-B when out_packed else row-major
   int out_packed;
+  int64_t out_plane;     // elements to the lo plane; 0: plain bf16 output
 };
 
 struct FinishArgs {
@@ -166,9 +176,9 @@ hipError_t launch_pack(int dtype, int kind, const void* src, const void* src2, v
 hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* tokens, int tok_src, const int* anchor,
                         int M, int T, int mask_id, float* x, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
-                          float eps, int M, int d, int row0, void* out, hipStream_t st);
-hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
-                            hipStream_t st);
+                          float eps, int M, int d, int row0, void* out, int64_t out_plane, hipStream_t st);
+hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
+                            const EpiArgs& ea, hipStream_t st);
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st);
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_finish(const FinishArgs& f, hipStream_t st);

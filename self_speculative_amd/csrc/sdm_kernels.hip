@@ -36,6 +36,9 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// Second term of the two-term bf16 expansion of x whose first term is hi
+// (x - hi is exact in fp32).
+__device__ __forceinline__ uint16_t f2bf_lo(float x, uint16_t hi) { return f2bf(x - bf2f(hi)); }
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -124,15 +127,16 @@ hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* token
 
 // ---------------------------------------------------------------------------
 // RMSNorm: y = (x / sqrt(mean(x^2) + eps)) * g.  One workgroup per row, fixed
-// reduction order.  bf16: rounded to bf16 straight into the packed B-operand
-// layout, 8 features (one 16-byte store) per thread and chunk.  f32: row-major.
+// reduction order.  bf16: written as hi/lo bf16 planes straight into the
+// packed B-operand layout, 8 features (one 16-byte store per plane) per thread
+// and chunk.  f32: row-major.
 // ---------------------------------------------------------------------------
 constexpr int kNormChunks = 4;  // chunks of 8 features per thread: d <= 8192
 
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, const float* __restrict__ part,
                                                       int nparts, int64_t part_stride,
                                                       const uint16_t* __restrict__ gain, float eps, int d, int row0,
-                                                      uint16_t* __restrict__ out) {
+                                                      uint16_t* __restrict__ out, int64_t out_plane) {
   const int m = blockIdx.x;
   float* xr = x + (int64_t)(row0 + m) * d;
   const int nch = d >> 3;
@@ -178,14 +182,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, con
     const int c = threadIdx.x + 256 * j;
     if (c < nch) {
       const u32x4 gv = ((const u32x4*)gain)[c];
-      u32x4 o;
+      u32x4 oh, ol;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float g0 = __uint_as_float(gv[e] << 16), g1 = __uint_as_float(gv[e] & 0xffff0000u);
-        const uint16_t lo = f2bf((v[j][2 * e] / r) * g0), hi = f2bf((v[j][2 * e + 1] / r) * g1);
-        o[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+        const float y0 = (v[j][2 * e] / r) * g0, y1 = (v[j][2 * e + 1] / r) * g1;
+        const uint16_t h0 = f2bf(y0), h1 = f2bf(y1);
+        oh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        ol[e] = (uint32_t)f2bf_lo(y0, h0) | ((uint32_t)f2bf_lo(y1, h1) << 16);
       }
-      *(u32x4*)(out + packed_index(m, 8 * c, d)) = o;
+      const int64_t pi = packed_index(m, 8 * c, d);
+      *(u32x4*)(out + pi) = oh;
+      *(u32x4*)(out + out_plane + pi) = ol;
     }
   }
 }
@@ -206,10 +214,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ x
 }
 
 hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
-                          float eps, int M, int d, int row0, void* out, hipStream_t st) {
+                          float eps, int M, int d, int row0, void* out, int64_t out_plane, hipStream_t st) {
   if (dtype == 1)
     SDM_LAUNCH(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, part, nparts, part_stride,
-                       (const uint16_t*)gain, eps, d, row0, (uint16_t*)out);
+                       (const uint16_t*)gain, eps, d, row0, (uint16_t*)out, out_plane);
   else
     SDM_LAUNCH(k_rmsnorm_f32, dim3(M), dim3(256), 0, st, x, (const float*)gain, eps, d, row0, (float*)out);
   return hipGetLastError();
@@ -323,6 +331,8 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
         uint16_t* q = ea.q_out + ((int64_t)m * Hq + head) * kHd;
         q[dl] = b1;
         q[dl + 64] = b2;
+        q[ea.q_plane + dl] = f2bf_lo(y1, b1);
+        q[ea.q_plane + dl + 64] = f2bf_lo(y2, b2);
       } else if (kblk) {
         kblk[kv_k_index(pk, dl)] = b1;
         kblk[kv_k_index(pk, dl + 64)] = b2;
@@ -354,7 +364,11 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
       const int f = 16 * nt + crow(r, h);
       const float g = c[r], u = c[r + 8];
       const float s = g / (1.f + expf(-g));
-      ea.h_out[packed_index(m, f, ea.F)] = f2bf(s * u);
+      const float y = s * u;
+      const uint16_t hb = f2bf(y);
+      const int64_t pi = packed_index(m, f, ea.F);
+      ea.h_out[pi] = hb;
+      ea.h_out[ea.h_plane + pi] = f2bf_lo(y, hb);
     }
   } else {  // EPI_LOGITS
     Rec a = rec_empty();
@@ -371,7 +385,9 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
 }
 
 // ---------------------------------------------------------------------------
-// Skinny bf16 GEMM  Y[m, n] = sum_k X[m, k] W[n, k]  (fp32 accumulate).
+// Skinny bf16 GEMM  Y[m, n] = sum_k X[m, k] W[n, k]  (fp32 accumulate), X
+// given as hi/lo planes: per 16-column block the hi product then the lo
+// product go into the same accumulator.
 // grid (NT, ceil(MTILES / MT)); WAVES waves per workgroup.  Workgroup nt owns
 // the 32-row weight tile nt over the whole K range; its waves take WAVES
 // contiguous K ranges, streaming the packed weights once (1 KiB per wave per
@@ -382,7 +398,8 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
 // ---------------------------------------------------------------------------
 template <int EPI, int MT, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
-                                                          const uint16_t* __restrict__ X, GemmShape g, EpiArgs ea) {
+                                                          const uint16_t* __restrict__ X, int64_t x_plane,
+                                                          GemmShape g, EpiArgs ea) {
   const int nt = blockIdx.x, sk = blockIdx.y, mg = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int mt0 = mg * MT;
@@ -403,29 +420,41 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
 
   const u32x4* wp = (const u32x4*)W + (int64_t)nt * g.KB * 64 + lane;
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
+  const u32x4* xq = xp + (x_plane >> 3);  // lo plane
   int kb = kb0;
   for (; kb + U <= kb1; kb += U) {
     u32x4 wv[U];
-    u32x4 xv[MT][U];
+    u32x4 xh[MT][U], xl[MT][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) wv[u] = __builtin_nontemporal_load(wp + (int64_t)(kb + u) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[i][u] = xp[((int64_t)i * g.KB + kb + u) * 64];
+        for (int u = 0; u < U; ++u) {
+          const int64_t o = ((int64_t)i * g.KB + kb + u) * 64;
+          xh[i][u] = xp[o];
+          xl[i][u] = xq[o];
+        }
       }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
-        if (i < mcount) acc[i] = mfma32(wv[u], xv[i][u], acc[i]);
+        if (i < mcount) {
+          acc[i] = mfma32(wv[u], xh[i][u], acc[i]);
+          acc[i] = mfma32(wv[u], xl[i][u], acc[i]);
+        }
   }
   for (; kb < kb1; ++kb) {
     const u32x4 wv = __builtin_nontemporal_load(wp + (int64_t)kb * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (i < mcount) acc[i] = mfma32(wv, xp[((int64_t)i * g.KB + kb) * 64], acc[i]);
+      if (i < mcount) {
+        const int64_t o = ((int64_t)i * g.KB + kb) * 64;
+        acc[i] = mfma32(wv, xp[o], acc[i]);
+        acc[i] = mfma32(wv, xq[o], acc[i]);
+      }
   }
 
   // reduction over the waves through LDS, one activation tile at a time
@@ -453,32 +482,33 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
 }
 
 template <int EPI, int WAVES>
-static void launch_gemm_w(const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea, hipStream_t st) {
+static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g, const EpiArgs& ea,
+                          hipStream_t st) {
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
   const dim3 grd(g.NT, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
   // split-K partial GEMMs stream with 8-deep batches (more waves resident per SIMD)
   constexpr int U1 = EPI == EPI_PARTIAL ? 8 : 16;
-  if (MT == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, g, ea);
-  else if (MT == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 8, WAVES>), grd, blk, 0, st, W, X, g, ea);
-  else SDM_LAUNCH((k_gemm_bf16<EPI, 4, 4, WAVES>), grd, blk, 0, st, W, X, g, ea);
+  if (MT == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  else if (MT == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  else SDM_LAUNCH((k_gemm_bf16<EPI, 4, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
 }
 
 template <int EPI>
-static hipError_t launch_gemm_epi(const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
-                                  hipStream_t st) {
-  if (g.WAVES == 8) launch_gemm_w<EPI, 8>(W, X, g, ea, st);
-  else launch_gemm_w<EPI, 4>(W, X, g, ea, st);
+static hipError_t launch_gemm_epi(const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
+                                  const EpiArgs& ea, hipStream_t st) {
+  if (g.WAVES == 8) launch_gemm_w<EPI, 8>(W, X, x_plane, g, ea, st);
+  else launch_gemm_w<EPI, 4>(W, X, x_plane, g, ea, st);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const GemmShape& g, const EpiArgs& ea,
-                            hipStream_t st) {
+hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
+                            const EpiArgs& ea, hipStream_t st) {
   switch (epi) {
-    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(W, X, g, ea, st);
-    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(W, X, g, ea, st);
-    case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(W, X, g, ea, st);
-    case EPI_PARTIAL: return launch_gemm_epi<EPI_PARTIAL>(W, X, g, ea, st);
-    default: return launch_gemm_epi<EPI_LOGITS>(W, X, g, ea, st);
+    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(W, X, x_plane, g, ea, st);
+    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(W, X, x_plane, g, ea, st);
+    case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(W, X, x_plane, g, ea, st);
+    case EPI_PARTIAL: return launch_gemm_epi<EPI_PARTIAL>(W, X, x_plane, g, ea, st);
+    default: return launch_gemm_epi<EPI_LOGITS>(W, X, x_plane, g, ea, st);
   }
 }
 
@@ -489,7 +519,8 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const
 // block row).  Wave w of the workgroup owns the 64 keys [j0 + 64w, j0 + 64w + 64)
 // -- exactly one KV page -- and loads that page's K and V blocks for head g
 // straight into registers (32 KiB, one burst).  Per 32-key tile: S^T = K Q^T
-// on MFMA (keys x query columns), an online softmax per column, then
+// on MFMA (keys x query columns; with QLO the query's hi and lo planes both
+// enter the product), an online softmax per column, then
 // O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts so the product
 // keeps ~16 bits of P.  The four waves' (max, sum, O) states are merged
 // through LDS in wave order and written as the split's partial; the combine
@@ -499,6 +530,7 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, const
 // Workgroups sharing a (split, head) pair get linear ids congruent mod 8 so
 // that they are placed on the same XCD and share its L2 for the K/V pages.
 // ---------------------------------------------------------------------------
+template <bool QLO>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   __shared__ float s_ml[4][2][32];
   __shared__ float s_o[4][kHd][32];
@@ -541,11 +573,17 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
   const int head = g * G + hl;
   const int qpos = n + t;
-  u32x4 qop[8];
+  u32x4 qop[8], qlo[QLO ? 8 : 1];
   {
-    const u32x4* qp = (const u32x4*)(a.q + ((int64_t)(slot * T + t) * a.Hq + head) * kHd);
+    const int64_t qo = ((int64_t)(slot * T + t) * a.Hq + head) * kHd;
+    const u32x4* qp = (const u32x4*)(a.q + qo);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) qop[kb] = cval ? qp[2 * kb + h] : u32x4{0, 0, 0, 0};
+    if constexpr (QLO) {
+      const u32x4* ql = (const u32x4*)(a.q + a.q_plane + qo);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) qlo[kb] = cval ? ql[2 * kb + h] : u32x4{0, 0, 0, 0};
+    }
   }
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[4];
@@ -558,7 +596,10 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     if (!wact || jt >= jw1) break;  // wave-uniform
     f32x16 sacc = f32x16{0};
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) sacc = mfma32(kv_k[kt * 8 + kb], qop[kb], sacc);
+    for (int kb = 0; kb < 8; ++kb) {
+      sacc = mfma32(kv_k[kt * 8 + kb], qop[kb], sacc);
+      if constexpr (QLO) sacc = mfma32(kv_k[kt * 8 + kb], qlo[kb], sacc);
+    }
     float sv[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -648,9 +689,10 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
 
 // Merge the splits for 32 query columns x 16 dims of one (slot, KV head):
 // o = sum_s w_s O_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s), split
-// order fixed; rounded to bf16.  The splits' (m, l) go to LDS with all 256
-// threads loading, the weights are formed there, then every thread sums two
-// (dim, column) outputs with its partial-O loads issued 8 splits at a time.
+// order fixed; written as bf16 (hi, plus the lo plane when out_plane is set).
+// The splits' (m, l) go to LDS with all 256 threads loading, the weights are
+// formed there, then every thread sums two (dim, column) outputs with its
+// partial-O loads issued 8 splits at a time.
 constexpr int kMaxSplits = 256;  // 65536 keys
 
 __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
@@ -706,8 +748,10 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
     for (; s < nsp; ++s) acc += s_m[s][col] * op[(int64_t)s * kHd * a.nq_pad];
     const float o = acc * inv;
     const int64_t k = (int64_t)(g * G + hl) * kHd + d;
-    if (a.out_packed) a.out[packed_index(m, k, K)] = f2bf(o);
-    else a.out[m * K + k] = f2bf(o);
+    const int64_t oi = a.out_packed ? packed_index(m, k, K) : m * K + k;
+    const uint16_t ob = f2bf(o);
+    a.out[oi] = ob;
+    if (a.out_plane) a.out[a.out_plane + oi] = f2bf_lo(o, ob);
   }
 }
 
@@ -715,7 +759,8 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
   const int pairs = grid_splits * a.kv.Hkv;
   const int grid = (pairs + 7) / 8 * 8 * nqt;
-  SDM_LAUNCH(k_attn_bf16, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
+  if (a.q_plane) SDM_LAUNCH(k_attn_bf16<true>, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
+  else SDM_LAUNCH(k_attn_bf16<false>, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {

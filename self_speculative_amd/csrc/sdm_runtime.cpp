@@ -66,6 +66,9 @@ struct Dims {
   int R, R32, max_pages, max_splits, max_slots, nq_cap;
   bool bf16;
   int64_t elt;
+  // bf16 path: elements from the hi plane to the lo plane of each activation buffer
+  int64_t xn_plane, q_plane, attn_plane, h_plane;
+  int planes;  // 2 for bf16 (hi, lo), 1 for f32
 };
 
 Dims dims_of(const sdm_config* c) {
@@ -79,6 +82,11 @@ Dims dims_of(const sdm_config* c) {
   D.nq_cap = D.G * D.R + 32 * D.max_slots;
   D.bf16 = c->dtype == SDM_BF16;
   D.elt = D.bf16 ? 2 : 4;
+  D.planes = D.bf16 ? 2 : 1;
+  D.xn_plane = (int64_t)D.R32 * D.d;
+  D.q_plane = (int64_t)D.R * D.qd;
+  D.attn_plane = (int64_t)D.R32 * D.qd;
+  D.h_plane = (int64_t)D.R32 * D.F;
   return D;
 }
 
@@ -98,10 +106,10 @@ Layout layout_of(const sdm_config* c) {
   };
   const int64_t rows_act = D.bf16 ? D.R32 : D.R;
   Lo.x = take((int64_t)D.R * D.d * 4);
-  Lo.xn = take(rows_act * D.d * D.elt);
-  Lo.q = take((int64_t)D.R * D.qd * D.elt);
-  Lo.attn = take(rows_act * D.qd * D.elt);
-  Lo.hbuf = take(rows_act * D.F * D.elt);
+  Lo.xn = take(D.planes * rows_act * D.d * D.elt);
+  Lo.q = take(D.planes * (int64_t)D.R * D.qd * D.elt);
+  Lo.attn = take(D.planes * rows_act * D.qd * D.elt);
+  Lo.hbuf = take(D.planes * rows_act * D.F * D.elt);
   int64_t ycols = 0;
   if (!D.bf16) ycols = std::max<int64_t>(std::max<int64_t>(D.qkv, 2LL * D.F), std::max<int64_t>(D.V, D.d));
   Lo.ybuf = take((int64_t)D.R * ycols * 4);
@@ -279,11 +287,13 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   ea.slots = sl;
   ea.Hq = D.Hq;
   ea.q_out = m->at<uint16_t>(m->lo.q);
+  ea.q_plane = D.q_plane;
   ea.rope_cos = m->at<float>(m->lo.rope_cos);
   ea.rope_sin = m->at<float>(m->lo.rope_sin);
   ea.x = x;
   ea.d = D.d;
   ea.h_out = m->at<uint16_t>(m->lo.hbuf);
+  ea.h_plane = D.h_plane;
   ea.F = D.F;
   ea.records = m->at<float4>(m->lo.records);
   ea.n_vtiles = (D.V + 31) / 32;
@@ -298,17 +308,18 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
     ea.kv = kv_view(m, l);
     { TimedScope ts(m, SDM_K_NORM);
       HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->attn_norm[l], eps, M, D.d, 0, xn,
-                             st),
+                             D.xn_plane, st),
               "rmsnorm"); }
     nparts = 0;
     if (D.bf16) {
       { TimedScope ts(m, SDM_K_QKV);
-      HIP_TRY(launch_gemm_bf16(EPI_QKV, (const uint16_t*)m->w_qkv[l], (const uint16_t*)xn,
+      HIP_TRY(launch_gemm_bf16(EPI_QKV, (const uint16_t*)m->w_qkv[l], (const uint16_t*)xn, D.xn_plane,
                                gemm_config(EPI_QKV, D.qkv, D.d, M),
                                ea, st),
               "qkv gemm"); }
       AttnArgs aa{};
       aa.q = ea.q_out;
+      aa.q_plane = D.q_plane;
       aa.kv = ea.kv;
       aa.slots = sl;
       aa.Hq = D.Hq;
@@ -320,6 +331,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       aa.nq_pad = (int)align_up((int64_t)D.G * sl.T, 32);
       aa.out = m->at<uint16_t>(m->lo.attn);
       aa.out_packed = 1;
+      aa.out_plane = D.attn_plane;
       int grid_splits = 0;
       for (int i = 0; i < sl.n_seq; ++i)
         grid_splits = std::max(grid_splits, (m->seqs[sl.ids[i]].len + sl.T + kAttnSplitKeys - 1) / kAttnSplitKeys);
@@ -330,21 +342,21 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       { TimedScope ts(m, SDM_K_O);
         const GemmShape go = gemm_config(EPI_PARTIAL, D.d, D.qd, M);
         nparts = go.S;
-        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_o[l], aa.out, go, ea, st),
+        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_o[l], aa.out, D.attn_plane, go, ea, st),
                 "o gemm"); }
       { TimedScope ts(m, SDM_K_NORM);
         HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->ffn_norm[l], eps, M, D.d, 0, xn,
-                               st),
+                               D.xn_plane, st),
                 "rmsnorm"); }
       nparts = 0;
       { TimedScope ts(m, SDM_K_GATE_UP);
-        HIP_TRY(launch_gemm_bf16(EPI_SWIGLU, (const uint16_t*)m->w_gu[l], (const uint16_t*)xn,
+        HIP_TRY(launch_gemm_bf16(EPI_SWIGLU, (const uint16_t*)m->w_gu[l], (const uint16_t*)xn, D.xn_plane,
                                  gemm_config(EPI_SWIGLU, 2 * D.F, D.d, M), ea, st),
                 "gate/up gemm"); }
       { TimedScope ts(m, SDM_K_DOWN);
         const GemmShape gd = gemm_config(EPI_PARTIAL, D.d, D.F, M);
         nparts = gd.S;
-        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_down[l], ea.h_out, gd, ea, st),
+        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_down[l], ea.h_out, D.h_plane, gd, ea, st),
                 "down gemm"); }
     } else {
       float* y = m->at<float>(m->lo.ybuf);
@@ -357,7 +369,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       HIP_TRY(launch_attention_f32(qf, ea.kv, sl, D.Hq, mode, af, st), "attention");
       HIP_TRY(launch_gemm_f32(af, (const float*)m->w_o[l], M, D.d, D.qd, y, st), "o gemm");
       HIP_TRY(launch_resid_f32(y, x, M, D.d, st), "residual");
-      HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, nullptr, 0, 0, m->ffn_norm[l], eps, M, D.d, 0, xn, st), "rmsnorm");
+      HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, nullptr, 0, 0, m->ffn_norm[l], eps, M, D.d, 0, xn, 0, st), "rmsnorm");
       HIP_TRY(launch_gemm_f32((const float*)xn, (const float*)m->w_gu[l], M, 2 * D.F, D.d, y, st), "gate/up gemm");
       HIP_TRY(launch_swiglu_f32(y, hf, M, D.F, st), "swiglu");
       HIP_TRY(launch_gemm_f32(hf, (const float*)m->w_down[l], M, D.d, D.F, y, st), "down gemm");
@@ -367,13 +379,14 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   // final norm + LM head on the rows whose logits are needed
   const int ML = logits_last_only ? 1 : M;
   const int row0 = logits_last_only ? M - 1 : 0;
-  HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->final_norm, eps, ML, D.d, row0, xn, st),
+  HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->final_norm, eps, ML, D.d, row0, xn,
+                         D.xn_plane, st),
           "final rmsnorm");
   ea.M = ML;
   ea.logits = d_logits;
   if (D.bf16) {
     TimedScope ts(m, SDM_K_LM_HEAD);
-    HIP_TRY(launch_gemm_bf16(EPI_LOGITS, (const uint16_t*)m->lm_head, (const uint16_t*)xn,
+    HIP_TRY(launch_gemm_bf16(EPI_LOGITS, (const uint16_t*)m->lm_head, (const uint16_t*)xn, D.xn_plane,
                              gemm_config(EPI_LOGITS, D.V, D.d, ML),
                              ea, st),
             "lm head");
@@ -842,6 +855,8 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
   aa.nq_pad = (int)align_up((int64_t)(n_q_heads / n_kv_heads) * T, 32);
   aa.out = (uint16_t*)d_out;
   aa.out_packed = 0;
+  aa.q_plane = 0;    // the op takes plain bf16 queries
+  aa.out_plane = 0;  // and returns plain bf16
   if (e == hipSuccess) e = launch_attention_bf16(aa, aa.max_splits, st);
   if (e == hipSuccess) e = launch_attn_combine_bf16(aa, st);
   if (e != hipSuccess) return fail(SDM_ERR_DEVICE, "attention: %s", hipGetErrorString(e));

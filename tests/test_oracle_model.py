@@ -6,7 +6,10 @@
 * BIDIR mode equals an independent torch composition (F.linear, SDPA with an
   explicit mask, F.rms_norm, F.silu, complex-number RoPE).
 * On a bf16 shape, the oracle's rounding points equal the same composition
-  with torch's own bf16 casts at those points.
+  with torch's own bf16 casts at those points: a single bf16 cast for k and v
+  (the KV cache), a two-term cast (hi, then the residual) for the activations
+  handed between kernels.  Moving either kind of point to the other rounding
+  is detected.
 """
 import dataclasses
 
@@ -84,9 +87,11 @@ def test_causal_forward_with_cache_equals_transformers_llama():
     np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
 
 
-def _torch_forward(shape, w, prefix, block, bidir, rnd):
+def _torch_forward(shape, w, prefix, block, bidir, rnd, rnd_kv=None):
     """Independent composition: whole sequence prefix+block in one pass, with
-    the block's mask rule built by loops; rnd(x) is the storage rounding."""
+    the block's mask rule built by loops; rnd(x) is the storage rounding of the
+    activations, rnd_kv(x) that of k and v (default: rnd)."""
+    rnd_kv = rnd if rnd_kv is None else rnd_kv
     d, hd, Hq, Hkv = shape.d_model, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     toks = np.concatenate([prefix, block]).astype(np.int64)
     n, T = len(prefix), len(block)
@@ -115,8 +120,8 @@ def _torch_forward(shape, w, prefix, block, bidir, rnd):
         qkv = _f64(shape, w, p + "w_qkv")
         a = rnd(F.rms_norm(h, (d,), eps=shape.rms_eps) * _f64(shape, w, p + "attn_norm"))
         q = rnd(rope(F.linear(a, qkv[: shape.q_dim]).view(S, Hq, hd)))
-        k = rnd(rope(F.linear(a, qkv[shape.q_dim: shape.q_dim + shape.kv_dim]).view(S, Hkv, hd)))
-        v = rnd(F.linear(a, qkv[shape.q_dim + shape.kv_dim:]).view(S, Hkv, hd))
+        k = rnd_kv(rope(F.linear(a, qkv[shape.q_dim: shape.q_dim + shape.kv_dim]).view(S, Hkv, hd)))
+        v = rnd_kv(F.linear(a, qkv[shape.q_dim + shape.kv_dim:]).view(S, Hkv, hd))
         G = Hq // Hkv
         o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1).repeat_interleave(G, 0),
                                            v.transpose(0, 1).repeat_interleave(G, 0), attn_mask=mask)
@@ -154,15 +159,26 @@ def test_block_forward_bf16_rounding_points(mode):
     m.forward(c, toks[:11], O.CAUSAL)
     c.n = 11
     ours = m.forward(c, toks[11:], mode)
-    rnd = lambda x: x.to(torch.bfloat16).to(torch.float64)
-    ref = _torch_forward(SMALL_BF16, w, toks[:11], toks[11:], mode == O.BIDIR, rnd)
+    one = lambda x: x.to(torch.bfloat16).to(torch.float64)
+
+    def two(x):
+        hi = one(x)
+        return hi + one(x - hi)
+
+    bidir = mode == O.BIDIR
+    ref = _torch_forward(SMALL_BF16, w, toks[:11], toks[11:], bidir, two, one)
     scale = np.abs(ref).max()
-    # torch casts float64 -> bf16 through float32 (double rounding), so a rare
-    # element lands one bf16 step away; that moves logits by ~1e-4 of scale.
-    np.testing.assert_allclose(ours, ref, rtol=0, atol=2e-3 * scale)
-    # ... while dropping the rounding points moves them by far more
-    no_r = _torch_forward(SMALL_BF16, w, toks[:11], toks[11:], mode == O.BIDIR, lambda x: x)
-    assert np.abs(no_r - ours).max() > 10 * np.abs(ref - ours).max()
+    # torch casts float64 -> bf16 through float32 (double rounding): a value
+    # within float32 resolution of a bf16 midpoint could land one step away.
+    tol = 2e-5 * scale
+    assert np.abs(ref - ours).max() <= tol
+    # each rounding point is visible: none at all, single bf16 for the
+    # activations too, no KV rounding, or no activation rounding all move the
+    # logits by far more (the last through k/v roundings that flip)
+    ident = lambda x: x
+    for act, kv in ((ident, ident), (one, one), (two, ident), (ident, one)):
+        other = _torch_forward(SMALL_BF16, w, toks[:11], toks[11:], bidir, act, kv)
+        assert np.abs(other - ours).max() > 10 * tol
 
 
 def test_row_independent_equals_batched():
