@@ -97,14 +97,23 @@ struct GemmShape {
   int MTILES;            // 32-row tiles of the activations
   int S;                 // workgroups splitting K (EPI_PARTIAL only)
   int WAVES;             // waves per workgroup, splitting the workgroup's K range
+  int TP;                // weight tiles per workgroup (one activation tile only)
 };
 
-// Launch configuration of a weight matrix: a function of the matrix shape and
-// its epilogue only (never of the number of rows), so that the summation order
-// -- and therefore every row's result -- does not depend on the batch.
-// Matrices whose outputs are summed into the residual stream (EPI_PARTIAL) are
-// split over S workgroups along K until the grid covers the chip; each split
-// writes an fp32 partial that the following RMSNorm adds in split order.
+constexpr int kGemmTargetGroups = 256;  // one workgroup per compute unit
+constexpr int kMaxSplitK = 8;           // split-K partial planes the RMSNorm adds
+
+// Launch configuration of a weight matrix.  The summation order of an output
+// -- the K split S, the waves' K ranges and their reduction order -- is a
+// function of the matrix shape and its epilogue only (never of the number of
+// rows), so every row's result is independent of the batch.  Matrices whose
+// outputs are summed into the residual stream (EPI_PARTIAL) are split over S
+// workgroups along K so that the grid covers the chip; each split writes an
+// fp32 partial that the following RMSNorm adds in split order.
+// TP only chooses which workgroup computes which tile: with a single
+// activation tile a workgroup takes TP weight tiles, so the activations it
+// reads from L2 are shared by TP weight streams while about one workgroup per
+// compute unit remains.
 inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   GemmShape g;
   g.NT = N / 32;
@@ -112,10 +121,16 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   g.MTILES = (rows + 31) / 32;
   g.S = 1;
   if (epi == EPI_PARTIAL)
-    while (g.NT * g.S < 256 && g.KB % (2 * g.S) == 0 && g.KB / (2 * g.S) >= 64 && g.S < 4) g.S *= 2;
-  if (g.NT >= 1024) g.WAVES = 4;
-  else if (g.KB / g.S >= 128) g.WAVES = 8;
-  else g.WAVES = 4;
+    while (g.NT * g.S < kGemmTargetGroups && g.KB % (2 * g.S) == 0 && g.KB / (2 * g.S) >= 32 && g.S < kMaxSplitK)
+      g.S *= 2;
+  g.WAVES = 4;
+  g.TP = 1;
+  if (g.MTILES == 1)
+    for (int t = 4; t > 1; --t)
+      if (g.NT % t == 0 && (g.NT / t) * g.S >= kGemmTargetGroups) {
+        g.TP = t;
+        break;
+      }
   return g;
 }
 

@@ -150,18 +150,23 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, con
       v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
       v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
       if (nparts > 0) {
-        // residual += sum of the split-K partials of the preceding projection (split order)
-        float pv[8];
+        // residual += sum of the split-K partials of the preceding projection
+        // (split order); every plane's loads are issued before the first add
         const float* pr = part + (int64_t)(row0 + m) * d + 8 * c;
-        {
-          const float4 pa = ((const float4*)pr)[0], pb = ((const float4*)pr)[1];
-          pv[0] = pa.x; pv[1] = pa.y; pv[2] = pa.z; pv[3] = pa.w; pv[4] = pb.x; pv[5] = pb.y; pv[6] = pb.z; pv[7] = pb.w;
-        }
-        for (int sp = 1; sp < nparts; ++sp) {
-          const float4 pa = ((const float4*)(pr + sp * part_stride))[0], pb = ((const float4*)(pr + sp * part_stride))[1];
-          pv[0] += pa.x; pv[1] += pa.y; pv[2] += pa.z; pv[3] += pa.w;
-          pv[4] += pb.x; pv[5] += pb.y; pv[6] += pb.z; pv[7] += pb.w;
-        }
+        float4 pa[kMaxSplitK], pb[kMaxSplitK];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplitK; ++sp)
+          if (sp < nparts) {
+            pa[sp] = ((const float4*)(pr + sp * part_stride))[0];
+            pb[sp] = ((const float4*)(pr + sp * part_stride))[1];
+          }
+        float pv[8] = {pa[0].x, pa[0].y, pa[0].z, pa[0].w, pb[0].x, pb[0].y, pb[0].z, pb[0].w};
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplitK; ++sp)
+          if (sp < nparts) {
+            pv[0] += pa[sp].x; pv[1] += pa[sp].y; pv[2] += pa[sp].z; pv[3] += pa[sp].w;
+            pv[4] += pb[sp].x; pv[5] += pb[sp].y; pv[6] += pb[sp].z; pv[7] += pb[sp].w;
+          }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[j][e] += pv[e];
         ((float4*)xr)[2 * c] = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
@@ -215,6 +220,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ x
 
 hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
                           float eps, int M, int d, int row0, void* out, int64_t out_plane, hipStream_t st) {
+  if (nparts < 0 || nparts > kMaxSplitK) return hipErrorInvalidValue;  // the kernel adds at most kMaxSplitK planes
   if (dtype == 1)
     SDM_LAUNCH(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, part, nparts, part_stride,
                        (const uint16_t*)gain, eps, d, row0, (uint16_t*)out, out_plane);
@@ -388,19 +394,23 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
 // Skinny bf16 GEMM  Y[m, n] = sum_k X[m, k] W[n, k]  (fp32 accumulate), X
 // given as hi/lo planes: per 16-column block the hi product then the lo
 // product go into the same accumulator.
-// grid (NT, ceil(MTILES / MT)); WAVES waves per workgroup.  Workgroup nt owns
-// the 32-row weight tile nt over the whole K range; its waves take WAVES
-// contiguous K ranges, streaming the packed weights once (1 KiB per wave per
-// load, non-temporal) and the activation tiles from L2.  The waves' partial
-// tiles are summed through LDS in wave order, so the summation order depends
-// only on (N, K, WAVES) -- never on the number of rows: every row's result is
-// independent of the batch it is computed in.
+// grid (NT / TP, S, ceil(MTILES / MT)); WAVES waves per workgroup.  Workgroup
+// x owns the TP consecutive 32-row weight tiles from TP * x over its K range
+// (split sk of S); its waves take WAVES contiguous pieces of that range,
+// streaming the packed weights once (1 KiB per tile per wave per load,
+// non-temporal) and the activation tiles from L2 -- read once for all TP
+// weight tiles.  The waves' partial tiles are summed through LDS in wave
+// order, so the summation order depends only on (N, K, S, WAVES) -- never on
+// the number of rows or on TP: every row's result is independent of the batch
+// it is computed in.  With TP > 1, wave t reduces and finishes tile t.
 // ---------------------------------------------------------------------------
-template <int EPI, int MT, int U, int WAVES>
+template <int EPI, int MT, int TP, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, int64_t x_plane,
                                                           GemmShape g, EpiArgs ea) {
-  const int nt = blockIdx.x, sk = blockIdx.y, mg = blockIdx.z;
+  static_assert(MT == 1 || TP == 1, "several weight tiles per workgroup only with one activation tile");
+  static_assert(TP <= WAVES, "one finishing wave per weight tile");
+  const int nt0 = blockIdx.x * TP, sk = blockIdx.y, mg = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int mt0 = mg * MT;
   const int mcount = min(MT, g.MTILES - mt0);
@@ -409,24 +419,28 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   const int kb0 = sk * kbs + min(kbs, wave * per);
   const int kb1 = sk * kbs + min(kbs, (wave + 1) * per);
 
-  f32x16 acc[MT];
+  f32x16 acc[MT][TP];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x16{0};
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < TP; ++t) acc[i][t] = f32x16{0};
 
   EpiPre pre;
   if constexpr (MT == 1) {
-    if (wave == 0) epi_preload<EPI>(pre, nt, mt0, lane, ea);
+    if (wave < TP) epi_preload<EPI>(pre, nt0 + wave, mt0, lane, ea);
   }
 
-  const u32x4* wp = (const u32x4*)W + (int64_t)nt * g.KB * 64 + lane;
+  const u32x4* wp = (const u32x4*)W + (int64_t)nt0 * g.KB * 64 + lane;  // tile nt0 + t at t * KB * 64
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
   int kb = kb0;
   for (; kb + U <= kb1; kb += U) {
-    u32x4 wv[U];
+    u32x4 wv[TP][U];
     u32x4 xh[MT][U], xl[MT][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wv[u] = __builtin_nontemporal_load(wp + (int64_t)(kb + u) * 64);
+    for (int t = 0; t < TP; ++t)
+#pragma unroll
+      for (int u = 0; u < U; ++u) wv[t][u] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb + u) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
@@ -440,43 +454,71 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (i < mcount) {
-          acc[i] = mfma32(wv[u], xh[i][u], acc[i]);
-          acc[i] = mfma32(wv[u], xl[i][u], acc[i]);
-        }
+      for (int t = 0; t < TP; ++t)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          if (i < mcount) {
+            acc[i][t] = mfma32(wv[t][u], xh[i][u], acc[i][t]);
+            acc[i][t] = mfma32(wv[t][u], xl[i][u], acc[i][t]);
+          }
   }
   for (; kb < kb1; ++kb) {
-    const u32x4 wv = __builtin_nontemporal_load(wp + (int64_t)kb * 64);
+    u32x4 wv[TP];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) wv[t] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
         const int64_t o = ((int64_t)i * g.KB + kb) * 64;
-        acc[i] = mfma32(wv, xp[o], acc[i]);
-        acc[i] = mfma32(wv, xq[o], acc[i]);
+        const u32x4 xh = xp[o], xl = xq[o];
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          acc[i][t] = mfma32(wv[t], xh, acc[i][t]);
+          acc[i][t] = mfma32(wv[t], xl, acc[i][t]);
+        }
       }
   }
 
-  // reduction over the waves through LDS, one activation tile at a time
-  __shared__ float red[WAVES][16][64];
+  if constexpr (MT == 1) {
+    // all TP tiles through LDS at once; wave t sums tile t over the waves in order
+    __shared__ float red[TP][WAVES][16][64];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    if (i >= mcount) break;
-    if (i > 0) __syncthreads();
+    for (int t = 0; t < TP; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[i][r];
+      for (int r = 0; r < 16; ++r) red[t][wave][r][lane] = acc[0][t][r];
     __syncthreads();
-    if (wave == 0) {
+    if (wave < TP) {
       float c[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = red[0][r][lane];
+        float v = red[wave][0][r][lane];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) v += red[w][r][lane];
+        for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
         c[r] = v;
       }
-      if constexpr (MT == 1) gemm_epilogue<EPI, true>(c, nt, mt0, lane, ea, pre);
-      else gemm_epilogue<EPI, false>(c, nt, mt0 + i, lane, ea, pre);
+      gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
+    }
+  } else {
+    // one activation tile at a time, wave 0 finishes
+    __shared__ float red[WAVES][16][64];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mcount) break;
+      if (i > 0) __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[i][0][r];
+      __syncthreads();
+      if (wave == 0) {
+        float c[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = red[0][r][lane];
+#pragma unroll
+          for (int w = 1; w < WAVES; ++w) v += red[w][r][lane];
+          c[r] = v;
+        }
+        gemm_epilogue<EPI, false>(c, nt0, mt0 + i, lane, ea, pre);
+      }
     }
   }
 }
@@ -485,12 +527,20 @@ template <int EPI, int WAVES>
 static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g, const EpiArgs& ea,
                           hipStream_t st) {
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
-  const dim3 grd(g.NT, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
-  // split-K partial GEMMs stream with 8-deep batches (more waves resident per SIMD)
-  constexpr int U1 = EPI == EPI_PARTIAL ? 8 : 16;
-  if (MT == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, U1, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
-  else if (MT == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
-  else SDM_LAUNCH((k_gemm_bf16<EPI, 4, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  const int TP = MT == 1 ? g.TP : 1;
+  const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
+  // weight loads in flight per wave: 16 tiles at TP 1, 4 * TP otherwise
+  constexpr int U1 = WAVES == 8 ? 8 : 16;
+  if (MT == 1) {
+    if (TP == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 1, U1, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 2, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 3) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 3, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_bf16<EPI, 1, 4, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  } else if (MT == 2) {
+    SDM_LAUNCH((k_gemm_bf16<EPI, 2, 1, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  } else {
+    SDM_LAUNCH((k_gemm_bf16<EPI, 4, 1, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  }
 }
 
 template <int EPI>
