@@ -58,6 +58,7 @@ struct Slots {
   int n_seq;   // sequences in this forward
   int T;       // rows per sequence
   int ids[kMaxSlots];
+  int len[kMaxSlots];  // committed length per slot: the block's first position
 };
 
 struct KvView {
@@ -66,7 +67,6 @@ struct KvView {
   int64_t layer_off;     // element offset of this layer inside a page
   const int* page_table; // [max_seqs][max_pages]
   int max_pages;
-  const int* seq_len;    // committed length per sequence (block base n)
   int Hkv, hd;
 };
 

@@ -281,7 +281,7 @@ __device__ __forceinline__ void epi_preload(EpiPre& p, int nt, int mt, int lane,
   if constexpr (EPI == EPI_QKV) {
     const int slot = m / ea.slots.T, t = m % ea.slots.T;
     const int seq = ea.slots.ids[slot];
-    p.pos = ea.kv.seq_len[seq] + t;
+    p.pos = ea.slots.len[slot] + t;
     p.page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + p.pos / kPageTokens];
     const int head = nt >> 2, s4 = nt & 3;
     if (head < ea.Hq + ea.kv.Hkv) {
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int seq = a.slots.ids[slot];
   const int T = a.slots.T;
-  const int n = a.kv.seq_len[seq];
+  const int n = a.slots.len[slot];
   const int nkeys = n + T;
   const int Hkv = a.kv.Hkv;
   const int G = a.Hq / Hkv;
@@ -752,13 +752,25 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
   const int ct = blockIdx.x, dch = blockIdx.y % (kHd / 16), g = blockIdx.y / (kHd / 16), slot = blockIdx.z;
   const int T = a.slots.T;
   const int Hkv = a.kv.Hkv, G = a.Hq / Hkv, nq = G * T;
-  const int seq = a.slots.ids[slot];
-  const int nkeys = a.kv.seq_len[seq] + T;
+  const int nkeys = a.slots.len[slot] + T;
   const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
   const int64_t b0 = ((int64_t)slot * Hkv + g) * a.max_splits;
   const int col = threadIdx.x & 31, row = threadIdx.x >> 5;
   const int c = ct * 32 + col;
   const bool cval = c < nq;
+  // this thread's partial outputs of the first kPre splits are requested
+  // before the (m, l) pass so that both round trips overlap
+  constexpr int kPre = 16;
+  const int64_t sstride = (int64_t)kHd * a.nq_pad;
+  float pre[2][kPre];
+  if (cval) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float* op = a.opart + (b0 * kHd + dch * 16 + row + 8 * j) * a.nq_pad + c;
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) pre[j][i] = i < nsp ? op[i * sstride] : 0.f;
+    }
+  }
   for (int s = row; s < nsp; s += 8) {
     s_m[s][col] = cval ? a.mlpart[((b0 + s) * 2) * a.nq_pad + c] : -INFINITY;
     s_l[s][col] = cval ? a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c] : 0.f;
@@ -787,15 +799,18 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
     const int d = dch * 16 + row + 8 * j;
     const float* op = a.opart + (b0 * kHd + d) * a.nq_pad + c;
     float acc = 0.f;
-    int s = 0;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      if (i < nsp) acc += s_m[i][col] * pre[j][i];
+    int s = kPre;
     for (; s + 8 <= nsp; s += 8) {
       float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = op[(int64_t)(s + i) * kHd * a.nq_pad];
+      for (int i = 0; i < 8; ++i) v[i] = op[(int64_t)(s + i) * sstride];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc += s_m[s + i][col] * v[i];
     }
-    for (; s < nsp; ++s) acc += s_m[s][col] * op[(int64_t)s * kHd * a.nq_pad];
+    for (; s < nsp; ++s) acc += s_m[s][col] * op[(int64_t)s * sstride];
     const float o = acc * inv;
     const int64_t k = (int64_t)(g * G + hl) * kHd + d;
     const int64_t oi = a.out_packed ? packed_index(m, k, K) : m * K + k;
@@ -941,7 +956,7 @@ __global__ void k_qkv_post_f32(const float* __restrict__ Y, EpiArgs ea, int hd) 
   const int ncols = (Hq + 2 * Hkv) * hd;
   const int slot = m / ea.slots.T, t = m % ea.slots.T;
   const int seq = ea.slots.ids[slot];
-  const int pos = ea.kv.seq_len[seq] + t;
+  const int pos = ea.slots.len[slot] + t;
   const int page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + pos / kPageTokens];
   const int pk = pos % kPageTokens;
   float* pool = (float*)ea.kv.pool;
@@ -983,7 +998,7 @@ __global__ void k_attn_f32(const float* __restrict__ q, KvView kv, Slots sl, int
   const int g = head * Hkv / Hq;
   const int slot = m / sl.T, t = m % sl.T;
   const int seq = sl.ids[slot];
-  const int n = kv.seq_len[seq];
+  const int n = sl.len[slot];
   const int last = (mode == BIDIR) ? n + sl.T - 1 : n + t;
   const float* pool = (const float*)kv.pool;
   const int* ptab = kv.page_table + (int64_t)seq * kv.max_pages;

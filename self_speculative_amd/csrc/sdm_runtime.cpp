@@ -92,7 +92,7 @@ Dims dims_of(const sdm_config* c) {
 
 struct Layout {
   int64_t x, xn, q, attn, hbuf, ybuf, part, opart, mlpart, records, tok, conf, margin, rope_cos, rope_sin,
-      page_table, seq_len, total;
+      page_table, total;
 };
 
 Layout layout_of(const sdm_config* c) {
@@ -128,7 +128,6 @@ Layout layout_of(const sdm_config* c) {
   Lo.rope_cos = take((int64_t)c->max_context * (D.hd / 2) * 4);
   Lo.rope_sin = take((int64_t)c->max_context * (D.hd / 2) * 4);
   Lo.page_table = take((int64_t)c->max_seqs * D.max_pages * 4);
-  Lo.seq_len = take((int64_t)c->max_seqs * 4);
   Lo.total = off;
   return Lo;
 }
@@ -212,9 +211,9 @@ sdm_status ensure_pages(sdm_model* m, const std::vector<int32_t>& seqs, const st
   return SDM_OK;
 }
 
+// Committed lengths live on the host and reach the kernels in Slots.
 sdm_status set_len(sdm_model* m, int32_t seq, int32_t len) {
   m->seqs[seq].len = len;
-  HIP_TRY(launch_set_ints(m->at<int>(m->lo.seq_len) + seq, &len, 1, m->stream), "length update");
   return SDM_OK;
 }
 
@@ -249,7 +248,6 @@ KvView kv_view(const sdm_model* m, int layer) {
   kv.layer_off = (int64_t)layer * 2 * m->D.Hkv * kPageTokens * m->D.hd;
   kv.page_table = m->at<int>(m->lo.page_table);
   kv.max_pages = m->D.max_pages;
-  kv.seq_len = m->at<int>(m->lo.seq_len);
   kv.Hkv = m->D.Hkv;
   kv.hd = m->D.hd;
   return kv;
@@ -261,7 +259,7 @@ struct TokenInput {
   const int* anchor = nullptr;  // TOK_DRAFT
 };
 
-// One forward over n_seq x T rows at positions seq_len[s] + t; writes K/V of
+// One forward over n_seq x T rows at positions len[s] + t; writes K/V of
 // the rows into the uncommitted slots; ends with the finish kernel.
 // logits_last_only: the LM head runs on the last row only (prefill chunks).
 sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInput& ti, bool logits_last_only,
@@ -408,11 +406,12 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   return SDM_OK;
 }
 
-Slots one_slot(int32_t seq, int T) {
+Slots one_slot(const sdm_model* m, int32_t seq, int T) {
   Slots s{};
   s.n_seq = 1;
   s.T = T;
   s.ids[0] = seq;
+  s.len[0] = m->seqs[seq].len;
   return s;
 }
 
@@ -437,6 +436,7 @@ sdm_status check_block_call(sdm_model* m, int32_t n_seq, const int32_t* h_ids, i
     if ((int64_t)m->seqs[s].len + B > m->cfg.max_context)
       return fail(SDM_ERR_CAPACITY, "sequence %d would exceed max_context", s);
     sl->ids[i] = s;
+    sl->len[i] = m->seqs[s].len;
     ids->push_back(s);
     ends->push_back(m->seqs[s].len + B);
   }
@@ -539,7 +539,6 @@ sdm_status sdm_init_model(const sdm_config* cfg, const sdm_weights* w, void* kv_
   hipError_t e = hipMemcpyAsync(m->ws + lo.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, m->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(m->ws + lo.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->stream);
-  if (e == hipSuccess) e = hipMemsetAsync(m->ws + lo.seq_len, 0, (size_t)cfg->max_seqs * 4, m->stream);
   // Attention reads whole 32-key tiles; slots past a sequence's end must hold
   // finite values (their probabilities are exactly 0), so the pool starts zeroed.
   if (e == hipSuccess)
@@ -626,14 +625,14 @@ sdm_status sdm_prefill(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32
     const bool last = off + T == n;
     FinishArgs fin{};
     fin.mode = FIN_NEXT;
-    fin.slots = one_slot(seq, 1);
+    fin.slots = one_slot(m, seq, 1);
     fin.T = 1;
     fin.next = d_next_token;
     TokenInput ti;
     ti.tokens = d_tokens + off;
     // intermediate chunks still run the (cheap, one-row) head so that every
     // chunk leaves the same state behind; only the last chunk's result counts
-    if ((s = forward(m, one_slot(seq, T), CAUSAL, ti, true, last ? d_logits : nullptr, fin)) != SDM_OK) return s;
+    if ((s = forward(m, one_slot(m, seq, T), CAUSAL, ti, true, last ? d_logits : nullptr, fin)) != SDM_OK) return s;
     if ((s = set_len(m, seq, off + T)) != SDM_OK) return s;
   }
   q.prefilled = true;
@@ -652,12 +651,12 @@ sdm_status sdm_decode_ar(sdm_model* m, int32_t seq, const int32_t* d_token, int3
   if ((s = ensure_pages(m, {seq}, {q.len + 1})) != SDM_OK) return s;
   FinishArgs fin{};
   fin.mode = FIN_NEXT;
-  fin.slots = one_slot(seq, 1);
+  fin.slots = one_slot(m, seq, 1);
   fin.T = 1;
   fin.next = d_next_token;
   TokenInput ti;
   ti.tokens = d_token;
-  if ((s = forward(m, one_slot(seq, 1), CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
+  if ((s = forward(m, one_slot(m, seq, 1), CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
   q.verified = 0;
   return set_len(m, seq, q.len + 1);
 }
@@ -789,21 +788,20 @@ size_t sdm_attn_pool_bytes(int32_t n_kv_heads, int32_t head_dim, int32_t n_pages
   return (size_t)n_pages * 2 * n_kv_heads * kPageTokens * head_dim * 2;
 }
 
-static int64_t attn_ws_layout(int32_t Hq, int32_t Hkv, int32_t T, int32_t max_keys, int64_t* o_ml, int64_t* o_len) {
+static int64_t attn_ws_layout(int32_t Hq, int32_t Hkv, int32_t T, int32_t max_keys, int64_t* o_ml) {
   const int G = Hq / Hkv;
   const int64_t nq_pad = align_up((int64_t)G * T, 32);
   const int64_t splits = (max_keys + kAttnSplitKeys - 1) / kAttnSplitKeys;
   const int64_t op = align_up(Hkv * splits * kHd * nq_pad * 4, 256);
   const int64_t ml = align_up(Hkv * splits * 2 * nq_pad * 4, 256);
   *o_ml = op;
-  *o_len = op + ml;
-  return op + ml + 256;
+  return op + ml;
 }
 
 size_t sdm_attn_workspace_bytes(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t T, int32_t max_keys) {
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || head_dim != kHd || T < 1 || max_keys < T) return 0;
-  int64_t a, b;
-  return (size_t)attn_ws_layout(n_q_heads, n_kv_heads, T, max_keys, &a, &b);
+  int64_t a;
+  return (size_t)attn_ws_layout(n_q_heads, n_kv_heads, T, max_keys, &a);
 }
 
 sdm_status sdm_attn_pack_kv(int32_t n_kv_heads, int32_t head_dim, const void* d_k, const void* d_v, int32_t n_keys,
@@ -826,13 +824,13 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
   if (n_prefix < 0 || T < 1 || T > 4096) return fail(SDM_ERR_ARG, "bad n_prefix / T");
   if ((int64_t)n_prefix + T > 65536) return fail(SDM_ERR_UNSUPPORTED, "more than 65536 keys");
   if (mode != SDM_CAUSAL && mode != SDM_BIDIR) return fail(SDM_ERR_ARG, "bad mode");
-  int64_t off_ml, off_len;
-  const int64_t need = attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml, &off_len);
+  int64_t off_ml;
+  const int64_t need = attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml);
   if ((int64_t)ws_bytes < need) return fail(SDM_ERR_CAPACITY, "attention workspace too small");
   hipStream_t st = (hipStream_t)hip_stream;
   char* ws = (char*)d_workspace;
   const int32_t nkeys = n_prefix + T;
-  hipError_t e = launch_set_ints((int*)(ws + off_len), &n_prefix, 1, st);
+  hipError_t e = hipSuccess;
   AttnArgs aa{};
   aa.q = (const uint16_t*)d_q;
   aa.kv.pool = (void*)d_pool;
@@ -840,12 +838,12 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
   aa.kv.layer_off = 0;
   aa.kv.page_table = d_pages;
   aa.kv.max_pages = (int)pages_for(nkeys, kPageTokens);
-  aa.kv.seq_len = (const int*)(ws + off_len);
   aa.kv.Hkv = n_kv_heads;
   aa.kv.hd = kHd;
   aa.slots.n_seq = 1;
   aa.slots.T = T;
   aa.slots.ids[0] = 0;
+  aa.slots.len[0] = n_prefix;
   aa.Hq = n_q_heads;
   aa.mode = mode;
   aa.scale = 1.f / sqrtf((float)kHd);
