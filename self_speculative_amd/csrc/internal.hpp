@@ -75,8 +75,9 @@ struct EpiArgs {
   Slots slots;
   KvView kv;
   int Hq;
-  uint16_t* q_out;       // QKV: [M][Hq][hd] hi plane, lo plane q_plane elements later
-  int64_t q_plane;
+  uint16_t* q_out;       // QKV, bf16: per (slot, KV head) a packed [q_nq_pad][hd] operand whose
+  int64_t q_plane;       //   column c = (q head within the group) * T + block row; hi plane,
+  int q_nq_pad;          //   lo plane q_plane elements later.  f32: row-major [M][Hq][hd]
   const float* rope_cos; // [max_context][hd/2]
   const float* rope_sin;
   float* x;              // RESID: residual [M][d]
@@ -135,8 +136,9 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
 }
 
 struct AttnArgs {
-  const uint16_t* q;     // [rows][Hq][hd] (row-major) hi plane
+  const uint16_t* q;     // q_packed: the QKV epilogue's packed layout; else row-major [rows][Hq][hd]
   int64_t q_plane;       // elements to the lo plane; 0: q is plain bf16
+  int q_packed;
   KvView kv;
   Slots slots;
   int Hq, mode;

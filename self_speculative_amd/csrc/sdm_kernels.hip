@@ -322,9 +322,10 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
       if (head < Hq + Hkv) kblk = pool + base + (int64_t)(head - Hq) * kPageTokens * kHd;
       else vblk = pool + base + (int64_t)(Hkv + head - Hq - Hkv) * kPageTokens * kHd;
     }
+    // registers r (dims dl) and r + 8 (dims dl + 64) after RoPE, rounded
+    uint16_t hb[16], lb[16];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int dl = 16 * s4 + crow(r, h);  // first-half dim; partner dim dl + 64 is c[r + 8]
       float y1 = c[r], y2 = c[r + 8];
       if (head < Hq + Hkv) {
         const float cs = pre.v[r], sn = pre.v[8 + r];
@@ -332,19 +333,39 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
         y1 = x1 * cs - x2 * sn;
         y2 = x2 * cs + x1 * sn;
       }
-      const uint16_t b1 = f2bf(y1), b2 = f2bf(y2);
-      if (head < Hq) {
-        uint16_t* q = ea.q_out + ((int64_t)m * Hq + head) * kHd;
-        q[dl] = b1;
-        q[dl + 64] = b2;
-        q[ea.q_plane + dl] = f2bf_lo(y1, b1);
-        q[ea.q_plane + dl + 64] = f2bf_lo(y2, b2);
-      } else if (kblk) {
-        kblk[kv_k_index(pk, dl)] = b1;
-        kblk[kv_k_index(pk, dl + 64)] = b2;
-      } else {
-        vblk[kv_v_index(pk, dl)] = b1;
-        vblk[kv_v_index(pk, dl + 64)] = b2;
+      hb[r] = f2bf(y1);
+      hb[r + 8] = f2bf(y2);
+      lb[r] = f2bf_lo(y1, hb[r]);
+      lb[r + 8] = f2bf_lo(y2, hb[r + 8]);
+    }
+    // registers 4i..4i+3 hold 4 consecutive dims, contiguous in the packed q
+    // and K layouts: one 8-byte store per group
+    auto pack4 = [](const uint16_t* v) {
+      return make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+    };
+    if (head < Hq) {
+      const int G = Hq / Hkv, T = ea.slots.T;
+      const int cq = (head % G) * T + m % T;  // query column within the KV head's group
+      uint16_t* q = ea.q_out + ((int64_t)(m / T) * Hkv + head / G) * ea.q_nq_pad * kHd;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 16 * s4 + crow(4 * (i & 1), h) + 64 * (i >> 1);
+        const int64_t pi = packed_index(cq, d0, kHd);
+        *(uint2*)(q + pi) = pack4(hb + 4 * i);
+        *(uint2*)(q + ea.q_plane + pi) = pack4(lb + 4 * i);
+      }
+    } else if (kblk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 16 * s4 + crow(4 * (i & 1), h) + 64 * (i >> 1);
+        *(uint2*)(kblk + kv_k_index(pk, d0)) = pack4(hb + 4 * i);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int dl = 16 * s4 + crow(r, h);
+        vblk[kv_v_index(pk, dl)] = hb[r];
+        vblk[kv_v_index(pk, dl + 64)] = hb[r + 8];
       }
     }
   } else if constexpr (EPI == EPI_RESID) {
@@ -580,7 +601,7 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64
 // Workgroups sharing a (split, head) pair get linear ids congruent mod 8 so
 // that they are placed on the same XCD and share its L2 for the K/V pages.
 // ---------------------------------------------------------------------------
-template <bool QLO>
+template <bool QLO, bool QPACK>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   __shared__ float s_ml[4][2][32];
   __shared__ float s_o[4][kHd][32];
@@ -624,7 +645,18 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int head = g * G + hl;
   const int qpos = n + t;
   u32x4 qop[8], qlo[QLO ? 8 : 1];
-  {
+  if constexpr (QPACK) {
+    // this query tile is 8 contiguous 1 KiB operand tiles (columns past nq
+    // hold stale values; their scores are masked)
+    const u32x4* qp = (const u32x4*)(a.q + ((int64_t)slot * Hkv + g) * a.nq_pad * kHd) + qt * 8 * 64 + lane;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qop[kb] = qp[kb * 64];
+    if constexpr (QLO) {
+      const u32x4* ql = qp + (a.q_plane >> 3);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) qlo[kb] = ql[kb * 64];
+    }
+  } else {
     const int64_t qo = ((int64_t)(slot * T + t) * a.Hq + head) * kHd;
     const u32x4* qp = (const u32x4*)(a.q + qo);
 #pragma unroll
@@ -824,8 +856,10 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
   const int pairs = grid_splits * a.kv.Hkv;
   const int grid = (pairs + 7) / 8 * 8 * nqt;
-  if (a.q_plane) SDM_LAUNCH(k_attn_bf16<true>, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
-  else SDM_LAUNCH(k_attn_bf16<false>, dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
+  if (a.q_plane && a.q_packed) SDM_LAUNCH((k_attn_bf16<true, true>), dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
+  else if (!a.q_plane && !a.q_packed)
+    SDM_LAUNCH((k_attn_bf16<false, false>), dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;  // hi/lo queries come packed, plain ones row-major
   return hipGetLastError();
 }
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {

@@ -84,7 +84,8 @@ Dims dims_of(const sdm_config* c) {
   D.elt = D.bf16 ? 2 : 4;
   D.planes = D.bf16 ? 2 : 1;
   D.xn_plane = (int64_t)D.R32 * D.d;
-  D.q_plane = (int64_t)D.R * D.qd;
+  // bf16: packed per (slot, KV head), at most nq_cap columns per head in all
+  D.q_plane = D.bf16 ? (int64_t)D.Hkv * D.nq_cap * D.hd : (int64_t)D.R * D.qd;
   D.attn_plane = (int64_t)D.R32 * D.qd;
   D.h_plane = (int64_t)D.R32 * D.F;
   return D;
@@ -107,7 +108,7 @@ Layout layout_of(const sdm_config* c) {
   const int64_t rows_act = D.bf16 ? D.R32 : D.R;
   Lo.x = take((int64_t)D.R * D.d * 4);
   Lo.xn = take(D.planes * rows_act * D.d * D.elt);
-  Lo.q = take(D.planes * (int64_t)D.R * D.qd * D.elt);
+  Lo.q = take(D.planes * D.q_plane * D.elt);
   Lo.attn = take(D.planes * rows_act * D.qd * D.elt);
   Lo.hbuf = take(D.planes * rows_act * D.F * D.elt);
   int64_t ycols = 0;
@@ -286,6 +287,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   ea.Hq = D.Hq;
   ea.q_out = m->at<uint16_t>(m->lo.q);
   ea.q_plane = D.q_plane;
+  ea.q_nq_pad = (int)align_up((int64_t)D.G * sl.T, 32);
   ea.rope_cos = m->at<float>(m->lo.rope_cos);
   ea.rope_sin = m->at<float>(m->lo.rope_sin);
   ea.x = x;
@@ -318,6 +320,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       AttnArgs aa{};
       aa.q = ea.q_out;
       aa.q_plane = D.q_plane;
+      aa.q_packed = 1;
       aa.kv = ea.kv;
       aa.slots = sl;
       aa.Hq = D.Hq;
@@ -853,7 +856,8 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
   aa.nq_pad = (int)align_up((int64_t)(n_q_heads / n_kv_heads) * T, 32);
   aa.out = (uint16_t*)d_out;
   aa.out_packed = 0;
-  aa.q_plane = 0;    // the op takes plain bf16 queries
+  aa.q_plane = 0;    // the op takes plain row-major bf16 queries
+  aa.q_packed = 0;
   aa.out_plane = 0;  // and returns plain bf16
   if (e == hipSuccess) e = launch_attention_bf16(aa, aa.max_splits, st);
   if (e == hipSuccess) e = launch_attn_combine_bf16(aa, st);
