@@ -14,7 +14,7 @@ constexpr int kMaxSlots = 64;          // sequences in one forward
 constexpr int kHd = 128;               // bf16 path head dim
 
 enum Mode { CAUSAL = 0, BIDIR = 1 };
-enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
+enum Epi { EPI_QKV = 0, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3 };
 enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1 };
 
@@ -80,8 +80,7 @@ struct EpiArgs {
   int q_nq_pad;          //   lo plane q_plane elements later.  f32: row-major [M][Hq][hd]
   const float* rope_cos; // [max_context][hd/2]
   const float* rope_sin;
-  float* x;              // RESID: residual [M][d]
-  int d;
+  int d;                 // PARTIAL: row length of the partial planes
   uint16_t* h_out;       // SWIGLU: packed-B [M32][F] hi plane, lo plane h_plane elements later
   int64_t h_plane;
   int F;

@@ -265,7 +265,7 @@ __device__ __forceinline__ Rec rec_unpack(const float4& v) { return Rec{v.x, __f
 // Epilogues of the bf16 GEMM.  c[16] is a 32x32 C tile in the MFMA layout:
 // column m = tile row-of-activations (lane % 32), rows crow(r, lane / 32).
 // EpiPre holds the epilogue's inputs that do not depend on the product (RoPE
-// cos/sin, the KV page, the residual values); the GEMM loads it before its K
+// cos/sin and the KV page); the GEMM loads it before its K
 // loop so those loads' latency hides behind the weight stream.
 // ---------------------------------------------------------------------------
 struct EpiPre {
@@ -292,10 +292,6 @@ __device__ __forceinline__ void epi_preload(EpiPre& p, int nt, int mt, int lane,
         p.v[8 + r] = ea.rope_sin[(int64_t)p.pos * (kHd / 2) + dl];
       }
     }
-  } else if constexpr (EPI == EPI_RESID) {
-    const float* xr = ea.x + (int64_t)m * ea.d + nt * 32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p.v[r] = xr[crow(r, h)];
   }
 }
 
@@ -367,16 +363,6 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
         vblk[kv_v_index(pk, dl)] = hb[r];
         vblk[kv_v_index(pk, dl + 64)] = hb[r + 8];
       }
-    }
-  } else if constexpr (EPI == EPI_RESID) {
-    if (!valid) return;
-    float* xr = ea.x + (int64_t)m * ea.d + nt * 32;
-    if constexpr (PRE) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xr[crow(r, h)] = pre_in.v[r] + c[r];
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xr[crow(r, h)] += c[r];
     }
   } else if constexpr (EPI == EPI_PARTIAL) {
     if (!valid) return;
@@ -576,7 +562,6 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64
                             const EpiArgs& ea, hipStream_t st) {
   switch (epi) {
     case EPI_QKV: return launch_gemm_epi<EPI_QKV>(W, X, x_plane, g, ea, st);
-    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(W, X, x_plane, g, ea, st);
     case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(W, X, x_plane, g, ea, st);
     case EPI_PARTIAL: return launch_gemm_epi<EPI_PARTIAL>(W, X, x_plane, g, ea, st);
     default: return launch_gemm_epi<EPI_LOGITS>(W, X, x_plane, g, ea, st);

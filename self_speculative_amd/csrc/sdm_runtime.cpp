@@ -290,7 +290,6 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   ea.q_nq_pad = (int)align_up((int64_t)D.G * sl.T, 32);
   ea.rope_cos = m->at<float>(m->lo.rope_cos);
   ea.rope_sin = m->at<float>(m->lo.rope_sin);
-  ea.x = x;
   ea.d = D.d;
   ea.h_out = m->at<uint16_t>(m->lo.hbuf);
   ea.h_plane = D.h_plane;
