@@ -102,6 +102,7 @@ struct GemmShape {
 
 constexpr int kGemmTargetGroups = 256;  // one workgroup per compute unit
 constexpr int kMaxSplitK = 8;           // split-K partial planes the RMSNorm adds
+constexpr int kGemmChunk = 4;           // k-blocks per round-robin chunk of a GEMM wave
 
 // Launch configuration of a weight matrix.  The summation order of an output
 // -- the K split S, the waves' K ranges and their reduction order -- is a

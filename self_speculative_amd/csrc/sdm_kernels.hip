@@ -131,9 +131,10 @@ hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* token
 // packed B-operand layout, 8 features (one 16-byte store per plane) per thread
 // and chunk.  f32: row-major.
 // ---------------------------------------------------------------------------
-constexpr int kNormChunks = 4;  // chunks of 8 features per thread: d <= 8192
+constexpr int kNormThreads = 512;                    // one workgroup per row
+constexpr int kNormChunks = 8192 / 8 / kNormThreads;  // chunks of 8 features per thread: d <= 8192
 
-__global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, const float* __restrict__ part,
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm_bf16(float* __restrict__ x, const float* __restrict__ part,
                                                       int nparts, int64_t part_stride,
                                                       const uint16_t* __restrict__ gain, float eps, int d, int row0,
                                                       uint16_t* __restrict__ out, int64_t out_plane) {
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, con
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kNormChunks; ++j) {
-    const int c = threadIdx.x + 256 * j;
+    const int c = threadIdx.x + kNormThreads * j;
     if (c < nch) {
       const float4 a = ((const float4*)xr)[2 * c], b = ((const float4*)xr)[2 * c + 1];
       v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
@@ -177,14 +178,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(float* __restrict__ x, con
     }
   }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  __shared__ float wsum[4];
+  __shared__ float wsum[kNormThreads / 64];
   if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  float tot = wsum[0];
+#pragma unroll
+  for (int w = 1; w < kNormThreads / 64; ++w) tot += wsum[w];
   const float r = sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int j = 0; j < kNormChunks; ++j) {
-    const int c = threadIdx.x + 256 * j;
+    const int c = threadIdx.x + kNormThreads * j;
     if (c < nch) {
       const u32x4 gv = ((const u32x4*)gain)[c];
       u32x4 oh, ol;
@@ -222,7 +225,7 @@ hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, in
                           float eps, int M, int d, int row0, void* out, int64_t out_plane, hipStream_t st) {
   if (nparts < 0 || nparts > kMaxSplitK) return hipErrorInvalidValue;  // the kernel adds at most kMaxSplitK planes
   if (dtype == 1)
-    SDM_LAUNCH(k_rmsnorm_bf16, dim3(M), dim3(256), 0, st, x, part, nparts, part_stride,
+    SDM_LAUNCH(k_rmsnorm_bf16, dim3(M), dim3(kNormThreads), 0, st, x, part, nparts, part_stride,
                        (const uint16_t*)gain, eps, d, row0, (uint16_t*)out, out_plane);
   else
     SDM_LAUNCH(k_rmsnorm_f32, dim3(M), dim3(256), 0, st, x, (const float*)gain, eps, d, row0, (float*)out);
@@ -403,13 +406,14 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
 // product go into the same accumulator.
 // grid (NT / TP, S, ceil(MTILES / MT)); WAVES waves per workgroup.  Workgroup
 // x owns the TP consecutive 32-row weight tiles from TP * x over its K range
-// (split sk of S); its waves take WAVES contiguous pieces of that range,
+// (split sk of S); its waves take that range in 4-block chunks, round robin,
 // streaming the packed weights once (1 KiB per tile per wave per load,
 // non-temporal) and the activation tiles from L2 -- read once for all TP
 // weight tiles.  The waves' partial tiles are summed through LDS in wave
 // order, so the summation order depends only on (N, K, S, WAVES) -- never on
-// the number of rows or on TP: every row's result is independent of the batch
-// it is computed in.  With TP > 1, wave t reduces and finishes tile t.
+// the number of rows, on TP or on the load batch U: every row's result is
+// independent of the batch it is computed in.  With TP > 1, wave t reduces and
+// finishes tile t.
 // ---------------------------------------------------------------------------
 template <int EPI, int MT, int TP, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
@@ -422,9 +426,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   const int mt0 = mg * MT;
   const int mcount = min(MT, g.MTILES - mt0);
   const int kbs = g.KB / g.S;  // this workgroup's K range: [sk * kbs, (sk + 1) * kbs)
-  const int per = (kbs + WAVES - 1) / WAVES;
-  const int kb0 = sk * kbs + min(kbs, wave * per);
-  const int kb1 = sk * kbs + min(kbs, (wave + 1) * per);
+  // The range goes to the waves in chunks of kGemmChunk k-blocks, round robin,
+  // so the workgroup's loads at any moment form one sequential stream; a wave
+  // sums its blocks in increasing order (blocks past the last whole chunk go
+  // round robin one at a time).  U only batches the loads.
+  static_assert(U % kGemmChunk == 0, "loads are batched in whole chunks");
+  const int kbase = sk * kbs;
+  const int nch = kbs / kGemmChunk;
+  constexpr int CB = U / kGemmChunk;                // chunks per load batch
+  constexpr int kstep = WAVES * kGemmChunk;         // from one of this wave's chunks to its next
+  const int kfull = kbase + nch * kGemmChunk;       // end of the whole chunks
+  // block u of a batch starting at this wave's chunk c: a compile-time offset
+  // from the batch's first block
+  auto boff = [](int u) { return (u / kGemmChunk) * WAVES * kGemmChunk + u % kGemmChunk; };
 
   f32x16 acc[MT][TP];
 #pragma unroll
@@ -440,20 +454,20 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   const u32x4* wp = (const u32x4*)W + (int64_t)nt0 * g.KB * 64 + lane;  // tile nt0 + t at t * KB * 64
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
-  int kb = kb0;
-  for (; kb + U <= kb1; kb += U) {
+  int kb = kbase + wave * kGemmChunk;  // first block of this wave's next chunk
+  for (; kb + (CB - 1) * kstep + kGemmChunk <= kfull; kb += CB * kstep) {
     u32x4 wv[TP][U];
     u32x4 xh[MT][U], xl[MT][U];
 #pragma unroll
     for (int t = 0; t < TP; ++t)
 #pragma unroll
-      for (int u = 0; u < U; ++u) wv[t][u] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb + u) * 64);
+      for (int u = 0; u < U; ++u) wv[t][u] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb + boff(u)) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t o = ((int64_t)i * g.KB + kb + u) * 64;
+          const int64_t o = ((int64_t)i * g.KB + kb + boff(u)) * 64;
           xh[i][u] = xp[o];
           xl[i][u] = xq[o];
         }
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
             acc[i][t] = mfma32(wv[t][u], xl[i][u], acc[i][t]);
           }
   }
-  for (; kb < kb1; ++kb) {
+  auto one_block = [&](int kb) {
     u32x4 wv[TP];
 #pragma unroll
     for (int t = 0; t < TP; ++t) wv[t] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb) * 64);
@@ -484,7 +498,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
           acc[i][t] = mfma32(wv[t], xl, acc[i][t]);
         }
       }
+  };
+  for (; kb + kGemmChunk <= kfull; kb += kstep) {
+#pragma unroll
+    for (int u = 0; u < kGemmChunk; ++u) one_block(kb + u);
   }
+  for (int b = nch * kGemmChunk + wave; b < kbs; b += WAVES) one_block(kbase + b);
 
   if constexpr (MT == 1) {
     // all TP tiles through LDS at once; wave t sums tile t over the waves in order
