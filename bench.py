@@ -44,11 +44,15 @@ def forward_bytes(s, n: int, T: int) -> int:
 
 def kernel_bytes(s, cls: str, M: int) -> int:
     """Algorithmic bytes of one launch of a GEMM class at M rows: weights +
-    activations in + activations out."""
+    activations in + activations out.  Activations handed between kernels are
+    two bf16 planes (4 bytes an element); k/v go to the cache as bf16; the O
+    and down projections' result is one fp32 residual update per element."""
     d, F = s.d_model, s.ffn_dim
     lw = layer_weight_bytes(s)
-    io = {"qkv": M * d * 2 + M * s.qkv_dim * 2, "o": M * s.q_dim * 2 + 2 * M * d * 4,
-          "gate_up": M * d * 2 + M * F * 2, "down": M * F * 2 + 2 * M * d * 4}
+    io = {"qkv": M * d * 4 + M * s.q_dim * 4 + M * 2 * s.kv_dim * 2,
+          "o": M * s.q_dim * 4 + M * d * 4,
+          "gate_up": M * d * 4 + M * F * 4,
+          "down": M * F * 4 + M * d * 4}
     return lw[cls] + io[cls]
 
 
@@ -188,7 +192,7 @@ def main() -> int:
             per[cls] = {"launches": n, "avg_us": round(tot_ms / max(1, n) * 1e3, 2), "min_us": round(mn * 1e3, 2),
                         "max_us": round(mx * 1e3, 2)}
             log(f"{cls:>12}: {n} launches, avg {per[cls]['avg_us']} us")
-        # roofline of the dominant kernel (gate/up GEMM: 47% of a forward's bytes)
+        # roofline of the dominant kernel (gate/up GEMM: 47% of a forward's weight bytes)
         gu = per["gate_up"]
         gu_bytes = kernel_bytes(s, "gate_up", B)
         achieved = gu_bytes / (gu["avg_us"] * 1e-6) / 1e9
