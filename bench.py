@@ -215,6 +215,43 @@ def main() -> int:
             kern[cls] = per[cls]
         kern["lm_head"]["GBps"] = round(s.vocab * s.d_model * 2 / (per["lm_head"]["avg_us"] * 1e-6) / 1e9, 1)
         out["kernels"] = kern
+        # per-forward latency by kind (HIP events around each call on the model's stream)
+        model.seq_reset(1)
+        first = prefill(model, 1, prompt)
+        run = SelfSpecRun(model, B, 1)
+        lat_sched = W.forced_accept_schedule(24, B, seed=3)
+        t_draft, t_verify = [], []
+        anchor_addr = first.data_ptr()
+        lb = torch.empty((24, B), dtype=torch.int32, device=dev)
+        la = torch.empty((24, B), dtype=torch.int32, device=dev)
+        acc = torch.empty(1, dtype=torch.int32, device=dev)
+        evs = []
+        for c in range(24):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            model.draft_block(1, anchor_addr, B, lb[c])
+            e[1].record()
+            model.verify_block([1], lb[c], B, la[c], acc)
+            e[2].record()
+            model.commit_kv(1, int(lat_sched[c]))
+            anchor_addr = la[c].data_ptr() + 4 * (int(lat_sched[c]) - 1)
+            evs.append(e)
+        ar_buf = torch.empty(33, dtype=torch.int32, device=dev)
+        ar_buf[0:1].copy_(la[23, int(lat_sched[23]) - 1:int(lat_sched[23])])
+        ar_ev = []
+        for t in range(1, 33):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            model.decode_ar(1, ar_buf.data_ptr() + 4 * (t - 1), ar_buf.data_ptr() + 4 * t)
+            e[1].record()
+            ar_ev.append(e)
+        torch.cuda.synchronize()
+        out["forward_latency"] = {
+            "bidir_M32": _pct([e[0].elapsed_time(e[1]) * 1e3 for e in evs]),
+            "causal_M32": _pct([e[1].elapsed_time(e[2]) * 1e3 for e in evs]),
+            "ar_M1": _pct([e[0].elapsed_time(e[1]) * 1e3 for e in ar_ev]),
+            "committed_len_range": [args.prompt, model.seq_length(1)]}
+        out["attention_op"] = attention_op_bench(log)
         # natural-accept self-spec and AR rates (short windows)
         model.seq_reset(1)
         first = prefill(model, 1, prompt)
@@ -263,6 +300,60 @@ def main() -> int:
     model.close()
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _pct(vals):
+    import numpy as np
+    a = np.asarray(vals, dtype=np.float64)
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def attention_op_bench(log) -> dict:
+    """The standalone block attention op (32 block rows, 32 q / 8 KV heads of
+    128, bf16, 64-token pages) over prefixes of 512, 4096 and 32768 keys in both
+    block masks: per-call latency from HIP events over 100 calls, and GB/s of
+    the algorithmic bytes (the K/V read once, q and the output)."""
+    import torch
+    import workloads as W
+    from self_speculative_amd import _lib as L
+    lib = L.lib()
+    dev = "cuda"
+    HQ, HKV, HD, T = 32, 8, 128, 32
+    st = torch.cuda.current_stream()
+    out = {}
+    for P in (512, 4096, 32768):
+        q, k, v = W.attention_op_inputs(P, T, HQ, HKV, HD, seed=0)
+        nkeys = P + T
+        n_pages = (nkeys + 63) // 64
+        pool = torch.zeros(lib.sdm_attn_pool_bytes(HKV, HD, n_pages), dtype=torch.uint8, device=dev)
+        pages = torch.arange(n_pages, dtype=torch.int32, device=dev)
+        tq, tk, tv = (torch.from_numpy(a.view("int16")).to(dev) for a in (q, k, v))
+        L.check(lib.sdm_attn_pack_kv(HKV, HD, tk.data_ptr(), tv.data_ptr(), nkeys, pages.data_ptr(), pool.data_ptr(),
+                                     st.cuda_stream))
+        wsb = lib.sdm_attn_workspace_bytes(HQ, HKV, HD, T, nkeys)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        o = torch.empty((T, HQ, HD), dtype=torch.int16, device=dev)
+        nbytes = nkeys * HKV * HD * 2 * 2 + 2 * T * HQ * HD * 2
+        for mode, name in ((1, "bidir"), (0, "causal")):
+            call = lambda: L.check(lib.sdm_attention(HQ, HKV, HD, tq.data_ptr(), pool.data_ptr(), pages.data_ptr(), P,
+                                                     T, mode, o.data_ptr(), ws.data_ptr(), wsb, st.cuda_stream))
+            for _ in range(10):
+                call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+            for e0, e1 in ev:
+                e0.record(st)
+                call()
+                e1.record(st)
+            torch.cuda.synchronize()
+            r = _pct([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+            r["GBps"] = round(nbytes / (r["median_us"] * 1e-6) / 1e9, 1)
+            r["hbm_frac"] = round(r["GBps"] / HBM_PEAK_GBS, 4)
+            r["bytes"] = nbytes
+            out[f"P{P}_{name}"] = r
+            log(f"attention op P={P} {name}: median {r['median_us']} us, {r['GBps']} GB/s")
+        del pool, ws, tk, tv, tq
+    return out
 
 
 def cpu_baseline(s, weights, prompt, tokens_per_cycle, log) -> dict:

@@ -12,6 +12,7 @@ constexpr int kPageTokens = 64;        // KV page size (positions per page)
 constexpr int kAttnSplitKeys = 256;    // keys per attention split (absolute ranges)
 constexpr int kMaxSlots = 64;          // sequences in one forward
 constexpr int kHd = 128;               // bf16 path head dim
+constexpr int kAttnStagedPairs = 256;  // (split, KV head) pairs from which attention stages splits in LDS
 
 enum Mode { CAUSAL = 0, BIDIR = 1 };
 enum Epi { EPI_QKV = 0, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };

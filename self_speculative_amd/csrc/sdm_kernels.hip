@@ -589,102 +589,51 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64
 
 // ---------------------------------------------------------------------------
 // Block attention, bf16, head_dim 128, over the paged cache.
-// One workgroup per (256-key split, KV head g, 32-column query tile) of a
-// sequence slot; the query columns of KV head g are (q head of the group,
-// block row).  Wave w of the workgroup owns the 64 keys [j0 + 64w, j0 + 64w + 64)
-// -- exactly one KV page -- and loads that page's K and V blocks for head g
-// straight into registers (32 KiB, one burst).  Per 32-key tile: S^T = K Q^T
-// on MFMA (keys x query columns; with QLO the query's hi and lo planes both
-// enter the product), an online softmax per column, then
-// O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts so the product
-// keeps ~16 bits of P.  The four waves' (max, sum, O) states are merged
-// through LDS in wave order and written as the split's partial; the combine
-// kernel merges splits in split order.  Masked keys contribute exact zeros and
-// every key range is an absolute range, so a row's result does not depend on
-// how many rows the block has.
-// Workgroups sharing a (split, head) pair get linear ids congruent mod 8 so
-// that they are placed on the same XCD and share its L2 for the K/V pages.
+// The unit of work is a 64-key page (one KV page of head g) against a query
+// tile of 32 columns; the query columns of KV head g are (q head of the
+// group, block row).  A page's state (max m, sum l, O) is formed by two
+// 32-key tiles: S^T = K Q^T on MFMA (keys x query columns; with QLO the
+// query's hi and lo planes both enter the product), an online softmax per
+// column, then O^T += V^T P^T on MFMA with P split into bf16 hi + lo parts so
+// the product keeps ~16 bits of P.  The four page states of a 256-key split
+// are merged in page order, pairwise (empty pages included), into the
+// split's partial; the combine kernel merges splits in split order.  Masked
+// keys contribute exact zeros and every key range is absolute, so a row's
+// result does not depend on how many rows the block has -- nor on which of
+// the two launch shapes below computed it:
+//   k_attn_bf16        one workgroup per (split, KV head, query tile); wave w
+//                      takes page w into registers, the page states meet in
+//                      LDS (short contexts: many small workgroups);
+//   k_attn_staged_bf16 one workgroup per (split, KV head); the four pages go
+//                      through LDS once and wave t runs query tile t over all
+//                      four (long contexts and batches).
 // ---------------------------------------------------------------------------
-template <bool QLO, bool QPACK>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-  __shared__ float s_ml[4][2][32];
-  __shared__ float s_o[4][kHd][32];
-  const int slot = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
-  const int seq = a.slots.ids[slot];
-  const int T = a.slots.T;
-  const int n = a.slots.len[slot];
-  const int nkeys = n + T;
-  const int Hkv = a.kv.Hkv;
-  const int G = a.Hq / Hkv;
-  const int nq = G * T;
-  const int nqt = (nq + 31) >> 5;
-  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
-  // linear id -> (pair = split * Hkv + g, query tile)
-  const int L = blockIdx.x;
-  const int qt = (L % (8 * nqt)) / 8;
-  const int pair = (L / (8 * nqt)) * 8 + (L % 8);
-  if (pair >= nsp * Hkv) return;
-  const int sp = pair / Hkv, g = pair % Hkv;
-  const int j0 = sp * kAttnSplitKeys;
-  const int jw = j0 + 64 * wave;  // this wave's page of keys
-  const bool wact = jw < nkeys;
+struct AttnState {
+  float m, l;
+  f32x16 o[4];  // O^T: dims dt * 32 + crow(r, h), this lane's query column
+};
+
+// State of one page (keys [jw, jw + 64)) for this lane's query column.
+// kop(i) / vop(i) give the page's K / V^T operand tile i for this lane.
+template <bool QLO, class KOp, class VOp>
+__device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp vop, const u32x4 (&qop)[8],
+                                                const u32x4 (&qlo)[QLO ? 8 : 1], int jw, int nkeys, int n,
+                                                int qpos, bool cval, int h, AttnState& st) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.o[i] = f32x16{0};
   const int jw1 = min(jw + 64, nkeys);
-
-  // K and V page blocks of head g for this wave's keys: 16 + 16 vectors per lane
-  u32x4 kv_k[16], kv_v[16];
-  if (wact) {
-    const int page = a.kv.page_table[(int64_t)seq * a.kv.max_pages + jw / kPageTokens];
-    const uint16_t* pb = (const uint16_t*)a.kv.pool + (int64_t)page * a.kv.page_elems + a.kv.layer_off;
-    const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
-    const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) kv_k[i] = kb[i * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) kv_v[i] = vb[i * 64 + lane];
-  }
-  const int c = qt * 32 + (lane & 31);
-  const bool cval = c < nq;
-  const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
-  const int head = g * G + hl;
-  const int qpos = n + t;
-  u32x4 qop[8], qlo[QLO ? 8 : 1];
-  if constexpr (QPACK) {
-    // this query tile is 8 contiguous 1 KiB operand tiles (columns past nq
-    // hold stale values; their scores are masked)
-    const u32x4* qp = (const u32x4*)(a.q + ((int64_t)slot * Hkv + g) * a.nq_pad * kHd) + qt * 8 * 64 + lane;
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) qop[kb] = qp[kb * 64];
-    if constexpr (QLO) {
-      const u32x4* ql = qp + (a.q_plane >> 3);
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) qlo[kb] = ql[kb * 64];
-    }
-  } else {
-    const int64_t qo = ((int64_t)(slot * T + t) * a.Hq + head) * kHd;
-    const u32x4* qp = (const u32x4*)(a.q + qo);
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) qop[kb] = cval ? qp[2 * kb + h] : u32x4{0, 0, 0, 0};
-    if constexpr (QLO) {
-      const u32x4* ql = (const u32x4*)(a.q + a.q_plane + qo);
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) qlo[kb] = cval ? ql[2 * kb + h] : u32x4{0, 0, 0, 0};
-    }
-  }
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{0};
-
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int jt = jw + 32 * kt;
-    if (!wact || jt >= jw1) break;  // wave-uniform
+    if (jt >= jw1) break;  // wave-uniform
     f32x16 sacc = f32x16{0};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      sacc = mfma32(kv_k[kt * 8 + kb], qop[kb], sacc);
-      if constexpr (QLO) sacc = mfma32(kv_k[kt * 8 + kb], qlo[kb], sacc);
+      const u32x4 kv = kop(kt * 8 + kb);
+      sacc = mfma32(kv, qop[kb], sacc);
+      if constexpr (QLO) sacc = mfma32(kv, qlo[kb], sacc);
     }
     float sv[16];
     float mx = -INFINITY;
@@ -696,8 +645,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       mx = fmaxf(mx, sv[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = (st.m == -INFINITY) ? 0.f : __expf(st.m - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -705,12 +654,12 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       psum += sv[r];
     }
     psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      for (int r = 0; r < 16; ++r) st.o[i][r] *= alpha;
 #pragma unroll
     for (int ka = 0; ka < 2; ++ka) {
       uint16_t hi[8], lo[8];
@@ -729,46 +678,214 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       const int kbv = 2 * kt + ka;  // 16-key group inside the page
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        o[dt] = mfma32(kv_v[dt * 4 + kbv], phi, o[dt]);
-        o[dt] = mfma32(kv_v[dt * 4 + kbv], plo, o[dt]);
+        const u32x4 vv = vop(dt * 4 + kbv);
+        st.o[dt] = mfma32(vv, phi, st.o[dt]);
+        st.o[dt] = mfma32(vv, plo, st.o[dt]);
       }
     }
   }
-  // merge the four waves' states (fixed wave order)
+}
+
+// Pairwise merge coefficients of a running state (m_a) with a page state
+// (m_b): the merged state is (max, a * l_a + b * l_b, a * O_a + b * O_b).
+__device__ __forceinline__ void attn_merge_coef(float m_a, float m_b, float& M, float& ca, float& cb) {
+  M = fmaxf(m_a, m_b);
+  ca = (m_a == -INFINITY) ? 0.f : __expf(m_a - M);
+  cb = (m_b == -INFINITY) ? 0.f : __expf(m_b - M);
+}
+
+// This lane's query tile operands (QPACK: the QKV epilogue's packed layout,
+// columns past nq hold stale values whose scores are masked; else row-major).
+template <bool QLO, bool QPACK>
+__device__ __forceinline__ void attn_load_q(const AttnArgs& a, int slot, int g, int qt, int t, int head, bool cval,
+                                            int lane, u32x4 (&qop)[8], u32x4 (&qlo)[QLO ? 8 : 1]) {
+  const int h = lane >> 5;
+  if constexpr (QPACK) {
+    const u32x4* qp = (const u32x4*)(a.q + ((int64_t)slot * a.kv.Hkv + g) * a.nq_pad * kHd) + qt * 8 * 64 + lane;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qop[kb] = qp[kb * 64];
+    if constexpr (QLO) {
+      const u32x4* ql = qp + (a.q_plane >> 3);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) qlo[kb] = ql[kb * 64];
+    }
+  } else {
+    const int64_t qo = ((int64_t)(slot * a.slots.T + t) * a.Hq + head) * kHd;
+    const u32x4* qp = (const u32x4*)(a.q + qo);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) qop[kb] = cval ? qp[2 * kb + h] : u32x4{0, 0, 0, 0};
+    if constexpr (QLO) {
+      const u32x4* ql = (const u32x4*)(a.q + a.q_plane + qo);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) qlo[kb] = cval ? ql[2 * kb + h] : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+__device__ __forceinline__ const uint16_t* attn_page_base(const AttnArgs& a, int seq, int jw) {
+  const int page = a.kv.page_table[(int64_t)seq * a.kv.max_pages + jw / kPageTokens];
+  return (const uint16_t*)a.kv.pool + (int64_t)page * a.kv.page_elems + a.kv.layer_off;
+}
+
+// Grid: linear id -> (pair = split * Hkv + g, query tile); workgroups sharing
+// a pair get linear ids congruent mod 8 so that they are placed on the same
+// XCD and share its L2 for the K/V pages.
+template <bool QLO, bool QPACK>
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
+  __shared__ float s_ml[4][2][32];
+  __shared__ float s_o[4][kHd][32];
+  const int slot = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int seq = a.slots.ids[slot];
+  const int T = a.slots.T;
+  const int n = a.slots.len[slot];
+  const int nkeys = n + T;
+  const int Hkv = a.kv.Hkv;
+  const int G = a.Hq / Hkv;
+  const int nq = G * T;
+  const int nqt = (nq + 31) >> 5;
+  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  const int L = blockIdx.x;
+  const int qt = (L % (8 * nqt)) / 8;
+  const int pair = (L / (8 * nqt)) * 8 + (L % 8);
+  if (pair >= nsp * Hkv) return;
+  const int sp = pair / Hkv, g = pair % Hkv;
+  const int jw = sp * kAttnSplitKeys + 64 * wave;  // this wave's page of keys
+
+  // K and V page blocks of head g for this wave's keys: 16 + 16 vectors per lane
+  u32x4 kv_k[16], kv_v[16];
+  if (jw < nkeys) {
+    const uint16_t* pb = attn_page_base(a, seq, jw);
+    const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
+    const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kv_k[i] = kb[i * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kv_v[i] = vb[i * 64 + lane];
+  }
+  const int c = qt * 32 + (lane & 31);
+  const bool cval = c < nq;
+  const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
+  u32x4 qop[8], qlo[QLO ? 8 : 1];
+  attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
+  AttnState st;
+  attn_page_state<QLO>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, nkeys, n,
+                       n + t, cval, h, st);
+  // the page states meet in LDS; per column, merged in page order
   if (h == 0) {
-    s_ml[wave][0][lane & 31] = m_run;
-    s_ml[wave][1][lane & 31] = l_run;
+    s_ml[wave][0][lane & 31] = st.m;
+    s_ml[wave][1][lane & 31] = st.l;
   }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_o[wave][dt * 32 + crow(r, h)][lane & 31] = o[dt][r];
+    for (int r = 0; r < 16; ++r) s_o[wave][dt * 32 + crow(r, h)][lane & 31] = st.o[dt][r];
   __syncthreads();
   const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
   const int col = threadIdx.x & 31;
   const int cc = qt * 32 + col;
   if (cc < nq) {
-    float M = -INFINITY;
+    float ca[4], cb[4];
+    float M = s_ml[0][0][col], Lsum = s_ml[0][1][col];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][col]);
-    float wgt[4];
-    float Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = s_ml[w][0][col];
-      wgt[w] = (mw == -INFINITY) ? 0.f : __expf(mw - M);
-      Lsum += wgt[w] * s_ml[w][1][col];
+    for (int w = 1; w < 4; ++w) {
+      float Mn;
+      attn_merge_coef(M, s_ml[w][0][col], Mn, ca[w], cb[w]);
+      Lsum = ca[w] * Lsum + cb[w] * s_ml[w][1][col];
+      M = Mn;
     }
     float* op = a.opart + base_idx * kHd * a.nq_pad;
     for (int d = threadIdx.x >> 5; d < kHd; d += 8) {
-      float v = 0.f;
+      float v = s_o[0][d][col];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += wgt[w] * s_o[w][d][col];
+      for (int w = 1; w < 4; ++w) v = ca[w] * v + cb[w] * s_o[w][d][col];
       op[(int64_t)d * a.nq_pad + cc] = v;
     }
     if (threadIdx.x < 32) {
       a.mlpart[(base_idx * 2 + 0) * a.nq_pad + cc] = M;
       a.mlpart[(base_idx * 2 + 1) * a.nq_pad + cc] = Lsum;
+    }
+  }
+}
+
+template <bool QLO, bool QPACK>
+__global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
+  __shared__ u32x4 s_k[4][16][64];  // the split's four pages: K operand tiles
+  __shared__ u32x4 s_v[4][16][64];  //                        and V^T operand tiles
+  const int slot = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int seq = a.slots.ids[slot];
+  const int T = a.slots.T;
+  const int n = a.slots.len[slot];
+  const int nkeys = n + T;
+  const int Hkv = a.kv.Hkv;
+  const int G = a.Hq / Hkv;
+  const int nq = G * T;
+  const int nqt = (nq + 31) >> 5;
+  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  const int pair = blockIdx.x;
+  if (pair >= nsp * Hkv) return;
+  const int sp = pair / Hkv, g = pair % Hkv;
+  {
+    const int jw = sp * kAttnSplitKeys + 64 * wave;  // wave w stages page w
+    if (jw < nkeys) {
+      const uint16_t* pb = attn_page_base(a, seq, jw);
+      const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
+      const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
+      u32x4 tk[16], tv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tk[i] = kb[i * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tv[i] = vb[i * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_k[wave][i][lane] = tk[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_v[wave][i][lane] = tv[i];
+    }
+  }
+  __syncthreads();
+  for (int qt = wave; qt < nqt; qt += 4) {
+    const int c = qt * 32 + (lane & 31);
+    const bool cval = c < nq;
+    const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
+    u32x4 qop[8], qlo[QLO ? 8 : 1];
+    attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
+    AttnState run, pg;
+    // page 0 starts the running state, pages 1..3 merge into it in order
+#pragma unroll 1
+    for (int w = 0; w < 4; ++w) {
+      const int jw = sp * kAttnSplitKeys + 64 * w;
+      AttnState& st = w == 0 ? run : pg;
+      // the page's 32 operand tiles come out of LDS in one burst
+      u32x4 pk[16], pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pk[i] = s_k[w][i][lane];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = s_v[w][i][lane];
+      attn_page_state<QLO>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, nkeys, n,
+                           n + t, cval, h, st);
+      if (w > 0) {
+        float M, ca, cb;
+        attn_merge_coef(run.m, pg.m, M, ca, cb);
+        run.l = ca * run.l + cb * pg.l;
+        run.m = M;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) run.o[dt][r] = ca * run.o[dt][r] + cb * pg.o[dt][r];
+      }
+    }
+    const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
+    if (cval) {
+      float* op = a.opart + base_idx * kHd * a.nq_pad + c;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) op[(int64_t)(dt * 32 + crow(r, h)) * a.nq_pad] = run.o[dt][r];
+      if (h == 0) {
+        a.mlpart[(base_idx * 2 + 0) * a.nq_pad + c] = run.m;
+        a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = run.l;
+      }
     }
   }
 }
@@ -859,11 +976,19 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st) {
   const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
   const int pairs = grid_splits * a.kv.Hkv;
-  const int grid = (pairs + 7) / 8 * 8 * nqt;
-  if (a.q_plane && a.q_packed) SDM_LAUNCH((k_attn_bf16<true, true>), dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
-  else if (!a.q_plane && !a.q_packed)
-    SDM_LAUNCH((k_attn_bf16<false, false>), dim3(grid, a.slots.n_seq), dim3(256), 0, st, a);
-  else return hipErrorInvalidValue;  // hi/lo queries come packed, plain ones row-major
+  // enough (split, head) pairs to cover the chip: stage each split once and
+  // run all its query tiles (same results as the tile-parallel shape)
+  const bool staged = (int64_t)pairs * a.slots.n_seq >= kAttnStagedPairs;
+  const dim3 grd(staged ? pairs : (pairs + 7) / 8 * 8 * nqt, a.slots.n_seq), blk(256);
+  if (a.q_plane && a.q_packed) {
+    if (staged) SDM_LAUNCH((k_attn_staged_bf16<true, true>), grd, blk, 0, st, a);
+    else SDM_LAUNCH((k_attn_bf16<true, true>), grd, blk, 0, st, a);
+  } else if (!a.q_plane && !a.q_packed) {
+    if (staged) SDM_LAUNCH((k_attn_staged_bf16<false, false>), grd, blk, 0, st, a);
+    else SDM_LAUNCH((k_attn_bf16<false, false>), grd, blk, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;  // hi/lo queries come packed, plain ones row-major
+  }
   return hipGetLastError();
 }
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {

@@ -201,6 +201,40 @@ def test_bf16_batch_independence(gm):
         np.testing.assert_array_equal(a, b)
 
 
+def test_bf16_staged_attention_matches_tile_parallel(weights, om):
+    """A batch with enough (split, KV head) pairs runs attention with each
+    256-key split staged once in LDS; alone, each sequence runs the
+    tile-parallel shape.  Both must give the same bits, and the oracle's
+    logits within the bar."""
+    from self_speculative_amd.model import Model
+    lens = [1900 + 37 * i for i in range(16)]           # 8+ splits x 2 KV heads x 16 = 256+ pairs
+    m = Model(SHAPE, weights, max_seqs=16, max_block=B, max_context=2560, max_rows=16 * B)
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    prompts = [W.prompt_ids(SHAPE, n, seed=31, index=i) for i, n in enumerate(lens)]
+    for i, p in enumerate(prompts):
+        m.prefill(i, _i32(p), nxt)
+    seqs = list(range(16))
+    blk = torch.full((16, B), SHAPE.mask_id, dtype=torch.int32, device=DEV)
+    nm = torch.empty(16, dtype=torch.int32, device=DEV)
+    lg = torch.empty((16 * B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+    print("bf16 staged attention: batch of 16", flush=True)
+    m.diffuse_step(seqs, blk, B, 0.9, False, nm, None, lg)
+    torch.cuda.synchronize()
+    batch = lg.cpu().numpy()
+    for i in (0, 9, 15):
+        print(f"bf16 staged attention: sequence {i} alone", flush=True)
+        b1 = torch.full((1, B), SHAPE.mask_id, dtype=torch.int32, device=DEV)
+        l1 = torch.empty((B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+        m.diffuse_step([i], b1, B, 0.9, False, nm[:1], None, l1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(l1.cpu().numpy(), batch[i * B:(i + 1) * B])
+    sess = O.OracleSession(om)
+    sess.prefill(0, prompts[15])
+    _, _, _, sel = sess.diffuse_step(0, np.full(B, SHAPE.mask_id, dtype=np.int32), 0.9, False)
+    assert np.abs(batch[15 * B:] - sel.logits).max() <= 2e-2
+    m.close()
+
+
 def test_bf16_shuffled_pages_bit_identical(weights):
     from self_speculative_amd.model import Model
     from self_speculative_amd import decode as D
