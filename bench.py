@@ -83,6 +83,8 @@ def main() -> int:
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline pass only (for profilers)")
+    ap.add_argument("--batch14b", action="store_true",
+                    help="also measure the 14B-shaped 16-sequence batched diffusion block (draws ~30 GB of weights)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -298,6 +300,10 @@ def main() -> int:
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(s, weights, prompt, tokens / K, log)
     model.close()
+    if args.batch14b:
+        del weights
+        torch.cuda.empty_cache()
+        out["batch_14b"] = batch14b_bench(log)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -353,6 +359,84 @@ def attention_op_bench(log) -> dict:
             out[f"P{P}_{name}"] = r
             log(f"attention op P={P} {name}: median {r['median_us']} us, {r['GBps']} GB/s")
         del pool, ws, tk, tv, tq
+    return out
+
+
+def batch14b_bench(log) -> dict:
+    """The 14B-shaped batched diffusion workload: 16 sequences, prompt lengths
+    uniform over {1024..8192} (seed 0), 64-token pages, block 32, tau 0.9 and at
+    most 8 denoising steps.  One block: every step and the causal commit
+    forward (M = 512 rows) timed with HIP events; each forward's algorithmic
+    HBM bytes (weights + KV read + KV written) and GEMM + attention flops
+    against the 8 TB/s and 2.5 PF/s (dense bf16) peaks."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from self_speculative_amd.decode import prefill
+    from self_speculative_amd.model import Model
+    s = W.SHAPES["14b"]
+    B, S_MAX, TAU, NSEQ = 32, 8, 0.9, 16
+    t0 = time.time()
+    w = W.make_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
+    lens = W.prompt_lengths(NSEQ, 1024, 8192, seed=0)
+    prompts = [W.prompt_ids(s, int(n), seed=0, index=i) for i, n in enumerate(lens)]
+    model = Model(s, w, max_seqs=NSEQ, max_block=B, max_context=8192 + 2 * B, max_rows=NSEQ * B, free_host=True)
+    del w
+    torch.cuda.synchronize()
+    log(f"14b batch: weights drawn and uploaded in {time.time() - t0:.1f}s")
+    dev = model.device
+    t0 = time.perf_counter()
+    for i, p in enumerate(prompts):
+        prefill(model, i, p)
+    torch.cuda.synchronize()
+    t_pf = time.perf_counter() - t0
+    seqs = list(range(NSEQ))
+    blk = torch.full((NSEQ, B), s.mask_id, dtype=torch.int32, device=dev)
+    nm = torch.empty(NSEQ, dtype=torch.int32, device=dev)
+    ar = torch.empty((NSEQ, B), dtype=torch.int32, device=dev)
+    acc = torch.empty(NSEQ, dtype=torch.int32, device=dev)
+    ev = []
+    t0 = time.perf_counter()
+    for step in range(S_MAX):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        model.diffuse_step(seqs, blk, B, TAU, step == S_MAX - 1, nm)
+        e[1].record()
+        ev.append(e)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    model.verify_block(seqs, blk, B, ar, acc)
+    e[1].record()
+    ev.append(e)
+    for q in seqs:
+        model.commit_kv(q, B)
+    torch.cuda.synchronize()
+    t_blk = time.perf_counter() - t0
+    assert int((blk == s.mask_id).sum().item()) == 0
+    fwd_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    wbytes = sum(layer_weight_bytes(s).values()) * s.n_layers + s.vocab * s.d_model * 2
+    kv_tok = s.n_layers * 2 * s.n_kv_heads * s.head_dim * 2
+    M = NSEQ * B
+    kv_read = int(sum(int(n) + B for n in lens)) * kv_tok
+    nbytes = wbytes + kv_read + M * kv_tok
+    params = wbytes // 2
+    attn_flops = 4 * sum(int(n) + B for n in lens) * B * s.n_q_heads * s.head_dim * s.n_layers
+    flops = 2 * M * params + attn_flops
+    med = float(np.median(fwd_us))
+    out = {"workload": "14B-shape decoder (40 layers, d 5120, 40/8 heads x 128, FFN 17408, vocab 151936), 16 sequences, "
+                       "prompt lengths U{1024..8192} seed 0, block 32, tau 0.9, at most 8 steps",
+           "prompt_tokens": int(lens.sum()), "prefill_s": round(t_pf, 3),
+           "prefill_tok_per_s": round(float(lens.sum()) / t_pf, 1),
+           "forward_us": {"median": round(med, 1), "min": round(min(fwd_us), 1), "max": round(max(fwd_us), 1),
+                          "n": len(fwd_us)},
+           "forward_bytes": nbytes, "forward_flops": flops,
+           "hbm_frac": round(nbytes / (med * 1e-6) / 8e12, 4),
+           "mfma_frac": round(flops / (med * 1e-6) / 2.5e15, 4),
+           "block_s": round(t_blk, 4),
+           "tokens_per_s": round(NSEQ * B / t_blk, 1)}
+    log(f"14b batch: forward median {med:.0f} us, HBM {out['hbm_frac']:.3f}, MFMA {out['mfma_frac']:.3f}, "
+        f"{out['tokens_per_s']} tok/s, prefill {out['prefill_tok_per_s']} tok/s")
+    model.close()
     return out
 
 

@@ -112,10 +112,9 @@ constexpr int kGemmChunk = 4;           // k-blocks per round-robin chunk of a G
 // outputs are summed into the residual stream (EPI_PARTIAL) are split over S
 // workgroups along K so that the grid covers the chip; each split writes an
 // fp32 partial that the following RMSNorm adds in split order.
-// TP only chooses which workgroup computes which tile: with a single
-// activation tile a workgroup takes TP weight tiles, so the activations it
-// reads from L2 are shared by TP weight streams while about one workgroup per
-// compute unit remains.
+// TP only chooses which workgroup computes which tile: a workgroup takes TP
+// weight tiles, so the activations it reads from L2 are shared by TP weight
+// streams while about one workgroup per compute unit remains.
 inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   GemmShape g;
   g.NT = N / 32;
@@ -131,12 +130,14 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   }
   g.WAVES = 4;
   g.TP = 1;
-  if (g.MTILES == 1)
-    for (int t = 4; t > 1; --t)
-      if (g.NT % t == 0 && (g.NT / t) * g.S >= kGemmTargetGroups) {
-        g.TP = t;
-        break;
-      }
+  const int mt = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);  // activation tiles per workgroup
+  const int mgroups = (g.MTILES + mt - 1) / mt;
+  const int tmax = mt == 4 ? 3 : 4;  // register budget: 4 x 4 accumulator tiles do not fit
+  for (int t = tmax; t > 1; --t)
+    if (g.NT % t == 0 && (g.NT / t) * g.S * mgroups >= kGemmTargetGroups) {
+      g.TP = t;
+      break;
+    }
   return g;
 }
 

@@ -419,7 +419,6 @@ template <int EPI, int MT, int TP, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, int64_t x_plane,
                                                           GemmShape g, EpiArgs ea) {
-  static_assert(MT == 1 || TP == 1, "several weight tiles per workgroup only with one activation tile");
   static_assert(TP <= WAVES, "one finishing wave per weight tile");
   const int nt0 = blockIdx.x * TP, sk = blockIdx.y, mg = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -525,25 +524,33 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
       gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
     }
   } else {
-    // one activation tile at a time, wave 0 finishes
-    __shared__ float red[WAVES][16][64];
+    // the MT x TP output tiles (activation tile major) go through LDS
+    // WAVES at a time; wave s sums tile q0 + s over the waves in order and
+    // finishes it
+    __shared__ float red[WAVES][WAVES][16][64];
+    const int ntile = mcount * TP;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if (i >= mcount) break;
-      if (i > 0) __syncthreads();
+    for (int q0 = 0; q0 < MT * TP; q0 += WAVES) {
+      if (q0 >= ntile) break;
+      if (q0 > 0) __syncthreads();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[i][0][r];
+      for (int qs = 0; qs < WAVES; ++qs)
+        if (q0 + qs < MT * TP && q0 + qs < ntile) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[qs][wave][r][lane] = acc[(q0 + qs) / TP][(q0 + qs) % TP][r];
+        }
       __syncthreads();
-      if (wave == 0) {
+      const int q = q0 + wave;
+      if (q < ntile) {
         float c[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = red[0][r][lane];
+          float v = red[wave][0][r][lane];
 #pragma unroll
-          for (int w = 1; w < WAVES; ++w) v += red[w][r][lane];
+          for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
           c[r] = v;
         }
-        gemm_epilogue<EPI, false>(c, nt0, mt0 + i, lane, ea, pre);
+        gemm_epilogue<EPI, false>(c, nt0 + q % TP, mt0 + q / TP, lane, ea, pre);
       }
     }
   }
@@ -553,7 +560,7 @@ template <int EPI, int WAVES>
 static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g, const EpiArgs& ea,
                           hipStream_t st) {
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
-  const int TP = MT == 1 ? g.TP : 1;
+  const int TP = g.TP;
   const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
   // weight loads in flight per wave: 16 tiles at TP 1, 4 * TP otherwise
   constexpr int U1 = WAVES == 8 ? 8 : 16;
@@ -563,17 +570,22 @@ static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane,
     else if (TP == 3) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 3, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
     else SDM_LAUNCH((k_gemm_bf16<EPI, 1, 4, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
   } else if (MT == 2) {
-    SDM_LAUNCH((k_gemm_bf16<EPI, 2, 1, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    if (TP == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 1, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 2, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 3) SDM_LAUNCH((k_gemm_bf16<EPI, 2, 3, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_bf16<EPI, 2, 4, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
   } else {
-    SDM_LAUNCH((k_gemm_bf16<EPI, 4, 1, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    if (TP == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 4, 1, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 4, 2, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_bf16<EPI, 4, 3, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
   }
 }
 
 template <int EPI>
 static hipError_t launch_gemm_epi(const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
                                   const EpiArgs& ea, hipStream_t st) {
-  if (g.WAVES == 8) launch_gemm_w<EPI, 8>(W, X, x_plane, g, ea, st);
-  else launch_gemm_w<EPI, 4>(W, X, x_plane, g, ea, st);
+  if (g.WAVES != 4) return hipErrorInvalidValue;  // every configuration runs four waves
+  launch_gemm_w<EPI, 4>(W, X, x_plane, g, ea, st);
   return hipGetLastError();
 }
 
