@@ -83,6 +83,8 @@ def main() -> int:
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline pass only (for profilers)")
+    ap.add_argument("--attention-op-only", action="store_true",
+                    help="run only the standalone attention op measurement (for profilers) and print it")
     ap.add_argument("--batch14b", action="store_true",
                     help="also measure the 14B-shaped 16-sequence batched diffusion block (draws ~30 GB of weights)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -104,6 +106,9 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+    if args.attention_op_only:
+        print(json.dumps({"attention_op": attention_op_bench(log)}), flush=True)
+        return 0
     s = W.SHAPES["8b"]
     B = 32
     t0 = time.time()
