@@ -113,3 +113,49 @@ def test_tiny_batch_diffusion_matches_single(gm, om):
     for i, p in enumerate(prompts):
         o = O.generate_diffusion(om, p, 24, 8, 0.0045, 4)
         assert outs[i].tokens == o.tokens and outs[i].steps_per_block == o.steps_per_block
+
+
+def test_tiny_vocab_reduction_planted_tie_and_mask_maximum():
+    """The LM head gets a later row b copying the draft's most frequent argmax
+    row a, and a MASK row 1.25 x row a.  On rows whose best non-MASK id is a
+    (with a positive logit) MASK holds the largest logit and b ties a exactly:
+    the selection must still return a -- MASK is excluded and a tie goes to the
+    lowest id -- on the GPU as in the oracle, with matching confidence."""
+    from self_speculative_amd.model import Model
+    mask, B = TINY.mask_id, 8
+    w = W.make_weights(TINY, seed=0)
+    p = W.prompt_ids(TINY, 12, seed=8)
+    sess = O.OracleSession(O.OracleModel(TINY, w))
+    g = int(sess.prefill(0, p).tok[0])
+    _, sel0 = sess.draft_block(0, g, B)
+    vals, counts = np.unique(sel0.tok[1:], return_counts=True)
+    order = [int(v) for v in vals[np.argsort(-counts, kind="stable")] if int(v) + 1 < mask]
+    a = order[0]
+    b = a + 1
+    w2 = dict(w)
+    lm = w["lm_head"].copy()
+    lm[b] = lm[a]
+    lm[mask] = 1.25 * lm[a]
+    w2["lm_head"] = lm
+    sess = O.OracleSession(O.OracleModel(TINY, w2))
+    assert int(sess.prefill(0, p).tok[0]) == g
+    oblk, osel = sess.draft_block(0, g, B)
+    planted = [r for r in range(1, B) if osel.tok[r] == a and osel.logits[r, a] > 0]
+    assert planted, "the plant must reach at least one row"
+    for r in planted:
+        lg = osel.logits[r]
+        assert lg[mask] > lg[a] == lg[b] and lg[a] == np.delete(lg, mask).max()
+    m = Model(TINY, w2, max_seqs=2, max_block=B, max_context=128, max_rows=32)
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    m.prefill(0, torch.as_tensor(p, dtype=torch.int32, device="cuda"), nxt)
+    blk = torch.empty(B, dtype=torch.int32, device="cuda")
+    m.draft_block(0, nxt, B, blk)
+    conf = torch.empty(B, dtype=torch.float32, device="cuda")
+    m.row_stats(conf=conf)
+    torch.cuda.synchronize()
+    assert int(nxt.item()) == g
+    got = blk.cpu().numpy()
+    print(f"tiny planted selection: a={a} b={b} rows {planted}", flush=True)
+    np.testing.assert_array_equal(got, oblk)
+    np.testing.assert_allclose(conf.cpu().numpy()[1:], osel.conf[1:], rtol=1e-4)
+    m.close()

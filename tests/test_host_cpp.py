@@ -1,0 +1,24 @@
+"""Host-only C++ unit tests (no GPU): the KV page allocator, built with g++
+and the address / undefined-behaviour sanitizers, then run."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_page_pool_sanitized(tmp_path):
+    exe = str(tmp_path / "test_page_pool")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-I", os.path.join(ROOT, "self_speculative_amd", "csrc"),
+           os.path.join(ROOT, "tests", "cpp", "test_page_pool.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    # the sanitizer runtime need not come first among preloaded libraries
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
