@@ -12,7 +12,8 @@ temperature-0 invariant.  The diffusion trajectory beyond the per-step
 selection rule has no independent pin ("parity unpinned": the pages print no
 worked example); the per-step rule itself is pinned.
 """
-from .model import (BIDIR, CAUSAL, KVCache, OracleModel, apply_rope, attention, bf16_pair_round, bf16_round,
-                    decode_bf16_bits, rms_normalize, rope_tables, select_rows, silu, visible)
+from .model import (BIDIR, CAUSAL, INT4_GROUP, KVCache, OracleModel, apply_rope, attention, bf16_pair_round,
+                    bf16_round, decode_bf16_bits, dequant_int4, int4_codes, rms_normalize, rope_tables, select_rows,
+                    silu, visible)
 from .modes import (GenResult, OracleSession, RowSel, accept_length, generate_ar, generate_diffusion,
                     generate_diffusion_batch, generate_selfspec, unmask_rule)

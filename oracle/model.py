@@ -102,6 +102,31 @@ def decode_bf16_bits(b: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+INT4_GROUP = 128  # input columns sharing one scale
+
+
+def int4_codes(codes: np.ndarray) -> np.ndarray:
+    """Unpack 4-bit weight codes.  ``codes`` is uint8 [rows, cols/2]; byte j of
+    a row holds column 2j in its low nibble and column 2j+1 in its high nibble,
+    each a two's-complement integer in [-8, 7].  Returns int64 [rows, cols]."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    q = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.int64)
+    q[:, 0::2] = b & 15
+    q[:, 1::2] = b >> 4
+    return np.where(q >= 8, q - 16, q)
+
+
+def dequant_int4(codes: np.ndarray, scale_bits: np.ndarray, group: int = INT4_GROUP) -> np.ndarray:
+    """Weight-only 4-bit matrix (the w4a16 format of the DGX Spark row of
+    fintech-frontier-insights' hardware table, read as group-wise int4 with one
+    bf16 scale per output row and group of ``group`` input columns):
+    w[r, c] = s[r, c // group] * q[r, c], exact in float64.  ``scale_bits`` is
+    uint16 bf16 bits [rows, cols / group]."""
+    q = int4_codes(codes)
+    s = decode_bf16_bits(scale_bits)
+    return q * np.repeat(s, group, axis=1)
+
+
 def rms_normalize(h: np.ndarray, eps: float) -> np.ndarray:
     """h / sqrt(mean(h^2) + eps) along the last axis."""
     return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
@@ -220,7 +245,10 @@ class OracleModel:
     """The decoder as a pure function of (weights, tokens, positions, cache, mode).
 
     ``weights`` is the dict produced by ``workloads.make_weights`` (float32
-    arrays, or uint16 bf16 bits for bf16 shapes).  Layer weights are widened to
+    arrays, or uint16 bf16 bits for bf16 shapes) or by
+    ``workloads.make_w4_weights`` (the decoder's linear layers as 4-bit codes
+    ``<name>.codes`` plus bf16 scales ``<name>.scales``; they are dequantized
+    exactly, then used as any other weight).  Layer weights are widened to
     ``dtype`` lazily; ``cache_layers`` keeps them widened between forwards.
     """
 
@@ -251,18 +279,25 @@ class OracleModel:
         """Two-term bf16 storage of an activation handed between kernels."""
         return bf16_pair_round(x).astype(self.dtype, copy=False) if self.bf16 else x
 
+    def _matrix(self, name: str) -> np.ndarray:
+        """A weight matrix [out, in]: 4-bit codes are dequantized, bf16 widened."""
+        w = self._raw
+        if name + ".codes" in w:
+            return dequant_int4(w[name + ".codes"], w[name + ".scales"]).astype(self.dtype, copy=False)
+        return self._widen(w[name])
+
     def layer(self, l: int) -> LayerWeights:
         if l in self._layers:
             return self._layers[l]
         s, w, p = self.shape, self._raw, f"layers.{l}."
-        qkv = self._widen(w[p + "w_qkv"])
+        qkv = self._matrix(p + "w_qkv")
         lw = LayerWeights(
             attn_norm=self._widen(w[p + "attn_norm"]),
             wq=qkv[: s.q_dim], wk=qkv[s.q_dim: s.q_dim + s.kv_dim], wv=qkv[s.q_dim + s.kv_dim:],
-            wo=self._widen(w[p + "w_o"]),
+            wo=self._matrix(p + "w_o"),
             ffn_norm=self._widen(w[p + "ffn_norm"]),
-            wg=self._widen(w[p + "w_gate"]), wu=self._widen(w[p + "w_up"]),
-            wd=self._widen(w[p + "w_down"]),
+            wg=self._matrix(p + "w_gate"), wu=self._matrix(p + "w_up"),
+            wd=self._matrix(p + "w_down"),
         )
         if self.cache_layers:
             self._layers[l] = lw

@@ -35,7 +35,7 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 __all__ = [
-    "ModelShape", "SHAPES", "weight_specs", "make_weights", "prompt_ids",
+    "ModelShape", "SHAPES", "weight_specs", "make_weights", "make_w4_weights", "INT4_LINEARS", "prompt_ids",
     "forced_accept_schedule", "prompt_lengths", "attention_op_inputs",
     "bf16_bits_from_f32", "f32_from_bf16_bits", "STREAM_WEIGHTS",
 ]
@@ -47,6 +47,12 @@ STREAM_FORCED_L = 2
 STREAM_PROMPT_LENGTHS = 3
 STREAM_ATTN_OP = 4
 STREAM_GAINS = 5
+STREAM_W4 = 6
+
+# Decoder matrices stored as 4-bit codes by make_w4_weights (embedding and LM
+# head stay bf16).
+INT4_LINEARS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down")
+W4_GROUP = 128  # input columns per bf16 scale
 
 _CHUNK = 1 << 24  # elements per independently seeded chunk of a large tensor
 
@@ -178,6 +184,54 @@ def make_weights(shape: ModelShape, seed: int = 0, gains: str = "ones",
     if jobs:
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(lambda j: _fill_chunk(j[0], seed, j[1], shape.init_std, bf16, j[2], j[3]), jobs))
+    return out
+
+
+def _fill_w4_rows(codes: np.ndarray, scales: np.ndarray, seed: int, key: Tuple[int, ...], r0: int, r1: int):
+    g = _rng(seed, *key)
+    cols = codes.shape[1] * 2
+    z = g.standard_normal((r1 - r0, cols), dtype=np.float32)
+    q = np.clip(np.rint(z * np.float32(2.5)), -8, 7).astype(np.int8).view(np.uint8)
+    codes[r0:r1] = (q[:, 0::2] & 15) | ((q[:, 1::2] & 15) << 4)
+    sc = g.uniform(0.8, 1.25, size=(r1 - r0, cols // W4_GROUP)).astype(np.float32) * np.float32(0.008)
+    scales[r0:r1] = bf16_bits_from_f32(sc)
+
+
+def make_w4_weights(shape: ModelShape, seed: int = 0, gains: str = "ones",
+                    threads: int | None = None) -> Dict[str, np.ndarray]:
+    """Weights of a bf16 shape whose decoder matrices are 4-bit.
+
+    The embedding, the LM head and the gains are those of ``make_weights``.
+    Each matrix named in INT4_LINEARS, [out, in], becomes ``<name>.codes``,
+    uint8 [out, in/2] (column 2j in the low nibble of byte j, 2j+1 in the high
+    nibble, two's complement), and ``<name>.scales``, uint16 bf16 bits
+    [out, in/128].  Both are drawn directly: codes are a standard normal times
+    2.5, rounded and clipped to [-8, 7] (the bell shape of rounded Gaussian
+    weights), scales 0.008 * U(0.8, 1.25), so the weights' spread is about
+    0.02 as in the bf16 draw.
+    """
+    if shape.dtype != "bf16":
+        raise ValueError("4-bit weights need a bf16 shape")
+    specs = weight_specs(shape)
+    is_lin = lambda name: name.startswith("layers.") and name.split(".")[-1] in INT4_LINEARS
+    out = make_weights(shape, seed, gains, threads, only=[n for n, _, _ in specs if not is_lin(n)])
+    threads = threads or min(16, os.cpu_count() or 1)
+    jobs = []
+    for idx, (name, shp, _) in enumerate(specs):
+        if not is_lin(name):
+            continue
+        rows, cols = shp
+        if cols % W4_GROUP:
+            raise ValueError(f"{name}: {cols} input columns is not a multiple of {W4_GROUP}")
+        codes = np.empty((rows, cols // 2), dtype=np.uint8)
+        scales = np.empty((rows, cols // W4_GROUP), dtype=np.uint16)
+        step = max(1, _CHUNK // cols)
+        for c, r0 in enumerate(range(0, rows, step)):
+            jobs.append((codes, scales, (STREAM_W4, idx, c), r0, min(rows, r0 + step)))
+        out[name + ".codes"] = codes
+        out[name + ".scales"] = scales
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda j: _fill_w4_rows(j[0], j[1], seed, j[2], j[3], j[4]), jobs))
     return out
 
 
