@@ -31,11 +31,13 @@
  *     sdm_last_error().
  *   - A handle must not be used from two threads at once.
  *
- * Numerics.  bf16 models keep weights, normalised activations, q/k/v after
- * RoPE (hence the KV cache), the attention output and the SwiGLU product in
- * bf16 (round to nearest, ties to even); every contraction accumulates in
- * fp32; the residual stream and logits are fp32.  f32 models keep all of it
- * in fp32.  The MASK id never wins an argmax and is left out of the softmax.
+ * Numerics.  bf16 models keep the weights and k/v after RoPE (hence the KV
+ * cache) in bf16 (round to nearest, ties to even), and hand the normalised
+ * activations, q, the attention output and the SwiGLU product between
+ * kernels as two-term bf16 values (hi = bf16(x), lo = bf16(x - hi)); every
+ * contraction accumulates in fp32; the residual stream and logits are fp32.
+ * f32 models keep all of it in fp32.  The MASK id never wins an argmax and is
+ * left out of the softmax.
  */
 #ifndef SDM_H
 #define SDM_H
@@ -60,6 +62,17 @@ typedef enum {
 
 typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
 
+/* Storage of the decoder's QKV, O, gate/up and down matrices (bf16 models).
+ *   SDM_WEIGHTS_BF16: bf16 (sdm_pack_matrix).
+ *   SDM_WEIGHTS_INT4: weight-only 4-bit ("w4a16", the DGX Spark row of
+ *     fintech-frontier-insights' hardware table; the format is this library's
+ *     reading): two's-complement codes in [-8, 7] and one bf16 scale per
+ *     output row and group of 128 input columns, weight = scale * code
+ *     (sdm_pack_matrix_int4).  Activations stay as for bf16 weights; the
+ *     embedding and the LM head stay bf16.  Needs d_model and ffn_dim
+ *     multiples of 128. */
+typedef enum { SDM_WEIGHTS_BF16 = 0, SDM_WEIGHTS_INT4 = 1 } sdm_weight_format;
+
 typedef enum { SDM_CAUSAL = 0, SDM_BIDIR = 1 } sdm_attn_mode;
 
 /* Model and capacity description.
@@ -69,12 +82,13 @@ typedef enum { SDM_CAUSAL = 0, SDM_BIDIR = 1 } sdm_attn_mode;
  *   reserved MASK token (vocab - 1 in every shipped shape).  page_tokens must
  *   be 64.  max_rows bounds the rows of one forward (n_seq * block, or a
  *   prefill chunk); max_context (<= 65536) bounds a sequence's length (prompt + output
- *   + one block). */
+ *   + one block).  weight_format is an sdm_weight_format. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, mask_id;
   float rope_base, rms_eps;
   int32_t dtype;
   int32_t page_tokens, max_seqs, max_block, max_context, max_rows;
+  int32_t weight_format;
 } sdm_config;
 
 /* Device weights in the library's layout (see sdm_pack_matrix).  Gains are
@@ -86,7 +100,9 @@ typedef struct {
  *   w_qkv     packed SDM_PACK_QKV of [(Hq + 2 Hkv) * hd, d_model] (q rows, k rows, v rows)
  *   w_o       packed SDM_PACK_PLAIN of [d_model, Hq * hd]
  *   w_gate_up packed SDM_PACK_GATE_UP of gate [ffn, d_model] and up [ffn, d_model]
- *   w_down    packed SDM_PACK_PLAIN of [d_model, ffn]                                 */
+ *   w_down    packed SDM_PACK_PLAIN of [d_model, ffn]
+ * With SDM_WEIGHTS_INT4, w_qkv, w_o, w_gate_up and w_down are packed by
+ * sdm_pack_matrix_int4 with the same kinds.                                     */
 typedef struct {
   const void *embed, *final_norm, *lm_head;
   const void *const *attn_norm, *const *w_qkv, *const *w_o;
@@ -108,6 +124,24 @@ size_t sdm_packed_bytes(const sdm_config* cfg, int64_t rows, int64_t cols);
  * 2*rows rows.  A pure permutation: no arithmetic.  Enqueued on hip_stream. */
 sdm_status sdm_pack_matrix(const sdm_config* cfg, int32_t kind, const void* d_src, const void* d_src2,
                            void* d_dst, int64_t rows, int64_t cols, void* hip_stream);
+
+/* Bytes of a packed 4-bit [rows, cols] matrix (codes, then scales); 0 if the
+ * config is bad, rows % 32 != 0 or cols % 128 != 0.  For SDM_PACK_GATE_UP pass
+ * rows = 2 * ffn_dim, as for sdm_packed_bytes. */
+size_t sdm_packed_bytes_int4(const sdm_config* cfg, int64_t rows, int64_t cols);
+
+/* Rearrange a 4-bit [rows, cols] matrix (out-major) into the layout the 4-bit
+ * GEMM streams.  d_codes is uint8 [rows, cols / 2]: byte j of a row holds
+ * column 2j in its low nibble and column 2j + 1 in its high nibble, each a
+ * two's-complement code in [-8, 7].  d_scales is bf16 [rows, cols / 128].  For
+ * SDM_PACK_GATE_UP, d_codes / d_scales hold the gate matrix and d_codes2 /
+ * d_scales2 the up matrix, each [rows, cols].  A pure permutation (the same
+ * row order as sdm_pack_matrix); d_dst holds sdm_packed_bytes_int4 bytes.
+ * Needs a bf16 config, cols % 128 == 0 and rows % 32 == 0 (% 16 for gate/up);
+ * device pointers 4-byte aligned.  Enqueued on hip_stream. */
+sdm_status sdm_pack_matrix_int4(const sdm_config* cfg, int32_t kind, const void* d_codes, const void* d_scales,
+                                const void* d_codes2, const void* d_scales2, void* d_dst, int64_t rows, int64_t cols,
+                                void* hip_stream);
 
 /* Create a model.  kv_pool holds n_pages pages of sdm_kv_page_bytes; the
  * workspace holds ws_bytes >= sdm_workspace_bytes.  Uploads the RoPE table

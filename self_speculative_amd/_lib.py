@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libsdm.so")
 SDM_OK, SDM_ERR_ARG, SDM_ERR_STATE, SDM_ERR_CAPACITY, SDM_ERR_DEVICE, SDM_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "OK", -1: "ERR_ARG", -2: "ERR_STATE", -3: "ERR_CAPACITY", -4: "ERR_DEVICE", -5: "ERR_UNSUPPORTED"}
 SDM_F32, SDM_BF16 = 0, 1
+SDM_WEIGHTS_BF16, SDM_WEIGHTS_INT4 = 0, 1
 SDM_CAUSAL, SDM_BIDIR = 0, 1
 SDM_PACK_PLAIN, SDM_PACK_QKV, SDM_PACK_GATE_UP = 0, 1, 2
 KERNEL_CLASSES = {"qkv": 0, "attn": 1, "attn_combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6,
@@ -32,7 +33,7 @@ class SdmConfig(ctypes.Structure):
                 ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab", c_int32), ("mask_id", c_int32),
                 ("rope_base", c_float), ("rms_eps", c_float), ("dtype", c_int32),
                 ("page_tokens", c_int32), ("max_seqs", c_int32), ("max_block", c_int32),
-                ("max_context", c_int32), ("max_rows", c_int32)]
+                ("max_context", c_int32), ("max_rows", c_int32), ("weight_format", c_int32)]
 
 
 class SdmWeights(ctypes.Structure):
@@ -48,6 +49,9 @@ SIGNATURES = {
     "sdm_packed_bytes": (c_size_t, [POINTER(SdmConfig), c_int64, c_int64]),
     "sdm_pack_matrix": (c_int32, [POINTER(SdmConfig), c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int64,
                                   c_void_p]),
+    "sdm_packed_bytes_int4": (c_size_t, [POINTER(SdmConfig), c_int64, c_int64]),
+    "sdm_pack_matrix_int4": (c_int32, [POINTER(SdmConfig), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int64, c_int64, c_void_p]),
     "sdm_init_model": (c_int32, [POINTER(SdmConfig), POINTER(SdmWeights), c_void_p, c_int64, c_void_p, c_size_t,
                                  c_void_p, POINTER(c_void_p)]),
     "sdm_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),

@@ -98,7 +98,7 @@ struct GemmShape {
   int MTILES;            // 32-row tiles of the activations
   int S;                 // workgroups splitting K (EPI_PARTIAL only)
   int WAVES;             // waves per workgroup, splitting the workgroup's K range
-  int TP;                // weight tiles per workgroup (one activation tile only)
+  int TP;                // weight tiles per workgroup
 };
 
 constexpr int kGemmTargetGroups = 256;  // one workgroup per compute unit
@@ -133,6 +133,54 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   const int mt = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);  // activation tiles per workgroup
   const int mgroups = (g.MTILES + mt - 1) / mt;
   const int tmax = mt == 4 ? 3 : 4;  // register budget: 4 x 4 accumulator tiles do not fit
+  for (int t = tmax; t > 1; --t)
+    if (g.NT % t == 0 && (g.NT / t) * g.S * mgroups >= kGemmTargetGroups) {
+      g.TP = t;
+      break;
+    }
+  return g;
+}
+
+// 4-bit weights (w4a16): group-wise int4 codes, one bf16 scale per output
+// row and group of kW4Group input columns.  Packed layout of an [N, K] matrix
+// (N a multiple of 32, K of kW4Group), codes first, then scales at byte
+// offset w4_scale_offset(N, K):
+//   codes:  [N/32][K/128][part 2][lane 64][16 B].  Word j (4 B) of a lane's
+//           16 bytes in part p is k-block 4p + j of the group; its nibble e
+//           (bits 4e..4e+3, two's complement) is the weight at row
+//           32 * tile + lane % 32, column 128 * group + 16 * (4p + j) +
+//           8 * (lane / 32) + e -- the k order of the bf16 MFMA A operand.
+//   scales: [N/32][K/128][half 2][16] bf16: half h, entry r is the scale of
+//           row 32 * tile + crow(r, h), the rows that accumulator register r
+//           of a lane of half h holds.
+constexpr int kW4Group = 128;
+constexpr int kW4GroupBlocks = kW4Group / 16;  // k-blocks per scale group
+inline int64_t w4_scale_offset(int64_t N, int64_t K) { return ((N * K / 2) + 255) / 256 * 256; }
+inline int64_t w4_packed_bytes(int64_t N, int64_t K) { return w4_scale_offset(N, K) + N * (K / kW4Group) * 2; }
+
+// Launch configuration of a 4-bit matrix: gemm_config's split and tile choice,
+// with every split a whole number of scale groups and at most four
+// accumulator tiles per wave (MT * TP <= 4; the wave keeps a running total and
+// the current group's sum of each).  As for bf16, nothing depends on the
+// number of rows except which workgroup computes which tile.
+inline GemmShape gemm_config_w4(int epi, int N, int K, int rows) {
+  GemmShape g;
+  g.NT = N / 32;
+  g.KB = K / 16;
+  g.MTILES = (rows + 31) / 32;
+  g.S = 1;
+  if (epi == EPI_PARTIAL) {
+    auto ok = [&](int s) {
+      return s <= kMaxSplitK && g.KB % s == 0 && (g.KB / s) % kW4GroupBlocks == 0 && g.KB / s >= 32;
+    };
+    while (g.NT * g.S < kGemmTargetGroups && ok(2 * g.S)) g.S *= 2;
+    while (ok(2 * g.S) && g.KB / (2 * g.S) >= 96 && g.NT * 2 * g.S <= 4 * kGemmTargetGroups) g.S *= 2;
+  }
+  g.WAVES = 4;
+  g.TP = 1;
+  const int mt = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
+  const int mgroups = (g.MTILES + mt - 1) / mt;
+  const int tmax = 4 / mt;
   for (int t = tmax; t > 1; --t)
     if (g.NT % t == 0 && (g.NT / t) * g.S * mgroups >= kGemmTargetGroups) {
       g.TP = t;
@@ -200,6 +248,10 @@ hipError_t launch_embed(int dtype, const void* E, int d, int V, const int* token
                         int M, int T, int mask_id, float* x, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, float* x, const float* part, int nparts, int64_t part_stride, const void* gain,
                           float eps, int M, int d, int row0, void* out, int64_t out_plane, hipStream_t st);
+hipError_t launch_pack_w4(int kind, const void* codes, const void* scales, const void* codes2, const void* scales2,
+                          void* dst, int64_t rows, int64_t cols, int head_dim, hipStream_t st);
+hipError_t launch_gemm_w4(int epi, const uint8_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
+                          const EpiArgs& ea, hipStream_t st);
 hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
                             const EpiArgs& ea, hipStream_t st);
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st);

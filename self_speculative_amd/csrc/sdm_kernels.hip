@@ -600,6 +600,238 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* W, const uint16_t* X, int64
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit weights (w4a16): packing and GEMM.
+// The weight is scale * code with a two's-complement 4-bit code and one bf16
+// scale per output row and group of 128 inputs.  The GEMM feeds each code to
+// the bf16 MFMA as the exact bf16 integer it is, sums a group's products
+// (activation hi and lo planes, as for bf16 weights) from zero, and adds
+// scale * group sum to the running total in fp32: in exact arithmetic the
+// product of the activations with the dequantized matrix.
+// ---------------------------------------------------------------------------
+__global__ void k_pack_w4_codes(int kind, const uint32_t* __restrict__ src, int which, uint32_t* __restrict__ dst,
+                                int64_t rows, int64_t cols, int head_dim) {
+  const int64_t words = cols / 8;  // source words of 8 codes per row
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * words) return;
+  const int64_t r = i / words, c0 = (i % words) * 8;
+  const int64_t pr = pack_row(kind, r, rows, which, head_dim);
+  const int64_t G = cols / kW4Group, grp = c0 / kW4Group;
+  const int kb = (int)((c0 % kW4Group) / 16), half = (int)((c0 % 16) / 8);
+  const int64_t lane = (pr & 31) + 32 * half;
+  dst[((((pr >> 5) * G + grp) * 2 + kb / 4) * 64 + lane) * 4 + kb % 4] = src[i];
+}
+
+__global__ void k_pack_w4_scales(int kind, const uint16_t* __restrict__ src, int which, uint16_t* __restrict__ dst,
+                                 int64_t rows, int64_t G, int head_dim) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * G) return;
+  const int64_t r = i / G, grp = i % G;
+  const int64_t pr = pack_row(kind, r, rows, which, head_dim);
+  const int rr = (int)(pr & 31);
+  const int h = (rr >> 2) & 1, reg = 4 * (rr >> 3) + (rr & 3);  // crow(reg, h) == rr
+  dst[(((pr >> 5) * G + grp) * 2 + h) * 16 + reg] = src[i];
+}
+
+hipError_t launch_pack_w4(int kind, const void* codes, const void* scales, const void* codes2, const void* scales2,
+                          void* dst, int64_t rows, int64_t cols, int head_dim, hipStream_t st) {
+  const int64_t out_rows = kind == 2 ? 2 * rows : rows;
+  uint32_t* dc = (uint32_t*)dst;
+  uint16_t* ds = (uint16_t*)((uint8_t*)dst + w4_scale_offset(out_rows, cols));
+  const int64_t nc = rows * (cols / 8), ns = rows * (cols / kW4Group);
+  const dim3 blk(256), gc((unsigned)((nc + 255) / 256)), gs((unsigned)((ns + 255) / 256));
+  for (int which = 0; which < (kind == 2 ? 2 : 1); ++which) {
+    const void* c = which ? codes2 : codes;
+    const void* sc = which ? scales2 : scales;
+    SDM_LAUNCH(k_pack_w4_codes, gc, blk, 0, st, kind, (const uint32_t*)c, which, dc, rows, cols, head_dim);
+    SDM_LAUNCH(k_pack_w4_scales, gs, blk, 0, st, kind, (const uint16_t*)sc, which, ds, rows, cols / kW4Group,
+               head_dim);
+  }
+  return hipGetLastError();
+}
+
+// The 8 codes of one k-block of a lane (nibble e at bits 4e) as the bf16 MFMA
+// operand: 4 words, each two bf16 integers (element 2j low, 2j + 1 high).
+// A code converts to fp32 exactly, and its bf16 bits are the top half.
+__device__ __forceinline__ u32x4 w4_operand(uint32_t w) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q0 = (int)(w << (28 - 8 * j)) >> 28;
+    const int q1 = (int)(w << (24 - 8 * j)) >> 28;
+    r[j] = __builtin_amdgcn_perm(__float_as_uint((float)q1), __float_as_uint((float)q0), 0x07060302u);
+  }
+  return r;
+}
+
+// Scale r (0..15) of this lane's half from the two words of 8 bf16 each.
+__device__ __forceinline__ float w4_scale(const u32x4 (&s)[2], int r) {
+  const uint32_t u = s[r >> 3][(r >> 1) & 3];
+  return __uint_as_float((r & 1) ? (u & 0xffff0000u) : (u << 16));
+}
+
+// Grid (NT / TP, S, ceil(MTILES / MT)), 4 waves.  The workgroup's K range
+// goes to the waves by scale group, round robin; a wave adds its groups in
+// increasing order and the waves' totals meet in LDS in wave order, as in
+// k_gemm_bf16, so a row's result does not depend on the batch it is in.
+template <int EPI, int MT, int TP>
+__global__ __launch_bounds__(256) void k_gemm_w4(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Ws,
+                                                 const uint16_t* __restrict__ X, int64_t x_plane, GemmShape g,
+                                                 EpiArgs ea) {
+  constexpr int WAVES = 4, GB = kW4GroupBlocks;
+  static_assert(MT * TP <= 4, "a wave holds a total and a group sum per tile");
+  const int nt0 = blockIdx.x * TP, sk = blockIdx.y, mg = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
+  const int mt0 = mg * MT;
+  const int mcount = min(MT, g.MTILES - mt0);
+  const int kbs = g.KB / g.S;      // this workgroup's K range in k-blocks
+  const int G = g.KB / GB;         // scale groups of a row
+  const int g0 = sk * kbs / GB;    // first group of the range
+  const int ngr = kbs / GB;
+
+  f32x16 tot[MT][TP];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < TP; ++t) tot[i][t] = f32x16{0};
+
+  EpiPre pre;
+  if constexpr (MT == 1) {
+    if (wave < TP) epi_preload<EPI>(pre, nt0 + wave, mt0, lane, ea);
+  }
+
+  const u32x4* wc = (const u32x4*)Wc + lane;   // tile nt, group gr, part p at ((nt * G + gr) * 2 + p) * 64
+  const u32x4* ws = (const u32x4*)Ws + 2 * h;  // tile nt, group gr at (nt * G + gr) * 4
+  const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
+  const u32x4* xq = xp + (x_plane >> 3);  // lo plane
+  for (int gi = wave; gi < ngr; gi += WAVES) {
+    const int gr = g0 + gi;
+    u32x4 cw[TP][2], sw[TP][2];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      const int64_t tg = (int64_t)(nt0 + t) * G + gr;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        cw[t][p] = __builtin_nontemporal_load(wc + (tg * 2 + p) * 64);
+        sw[t][p] = ws[tg * 4 + p];
+      }
+    }
+    f32x16 acc[MT][TP];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int t = 0; t < TP; ++t) acc[i][t] = f32x16{0};
+#pragma unroll
+    for (int b = 0; b < GB; ++b) {
+      u32x4 xh[MT], xl[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        if (MT == 1 || i < mcount) {
+          const int64_t o = ((int64_t)i * g.KB + gr * GB + b) * 64;
+          xh[i] = xp[o];
+          xl[i] = xq[o];
+        }
+#pragma unroll
+      for (int t = 0; t < TP; ++t) {
+        const u32x4 a = w4_operand(cw[t][b >> 2][b & 3]);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          if (MT == 1 || i < mcount) {
+            acc[i][t] = mfma32(a, xh[i], acc[i][t]);
+            acc[i][t] = mfma32(a, xl[i], acc[i][t]);
+          }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TP; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sc = w4_scale(sw[t], r);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) tot[i][t][r] = __builtin_fmaf(sc, acc[i][t][r], tot[i][t][r]);
+      }
+  }
+
+  if constexpr (MT == 1) {
+    __shared__ float red[TP][WAVES][16][64];
+#pragma unroll
+    for (int t = 0; t < TP; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[t][wave][r][lane] = tot[0][t][r];
+    __syncthreads();
+    if (wave < TP) {
+      float c[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = red[wave][0][r][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
+        c[r] = v;
+      }
+      gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
+    }
+  } else {
+    __shared__ float red[WAVES][WAVES][16][64];
+    const int ntile = mcount * TP;
+#pragma unroll
+    for (int q0 = 0; q0 < MT * TP; q0 += WAVES) {
+      if (q0 >= ntile) break;
+      if (q0 > 0) __syncthreads();
+#pragma unroll
+      for (int qs = 0; qs < WAVES; ++qs)
+        if (q0 + qs < MT * TP && q0 + qs < ntile) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[qs][wave][r][lane] = tot[(q0 + qs) / TP][(q0 + qs) % TP][r];
+        }
+      __syncthreads();
+      const int q = q0 + wave;
+      if (q < ntile) {
+        float c[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = red[wave][0][r][lane];
+#pragma unroll
+          for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
+          c[r] = v;
+        }
+        gemm_epilogue<EPI, false>(c, nt0 + q % TP, mt0 + q / TP, lane, ea, pre);
+      }
+    }
+  }
+}
+
+template <int EPI>
+static hipError_t launch_gemm_w4_epi(const uint8_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
+                                     const EpiArgs& ea, hipStream_t st) {
+  const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
+  const int TP = g.TP;
+  if (g.WAVES != 4 || MT * TP > 4 || g.NT % TP || g.KB % (g.S * kW4GroupBlocks)) return hipErrorInvalidValue;
+  const uint16_t* Ws = (const uint16_t*)(W + w4_scale_offset((int64_t)g.NT * 32, (int64_t)g.KB * 16));
+  const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(256);
+  if (MT == 1) {
+    if (TP == 1) SDM_LAUNCH((k_gemm_w4<EPI, 1, 1>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else if (TP == 2) SDM_LAUNCH((k_gemm_w4<EPI, 1, 2>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else if (TP == 3) SDM_LAUNCH((k_gemm_w4<EPI, 1, 3>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_w4<EPI, 1, 4>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+  } else if (MT == 2) {
+    if (TP == 1) SDM_LAUNCH((k_gemm_w4<EPI, 2, 1>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_w4<EPI, 2, 2>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+  } else {
+    SDM_LAUNCH((k_gemm_w4<EPI, 4, 1>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4(int epi, const uint8_t* W, const uint16_t* X, int64_t x_plane, const GemmShape& g,
+                          const EpiArgs& ea, hipStream_t st) {
+  switch (epi) {
+    case EPI_QKV: return launch_gemm_w4_epi<EPI_QKV>(W, X, x_plane, g, ea, st);
+    case EPI_SWIGLU: return launch_gemm_w4_epi<EPI_SWIGLU>(W, X, x_plane, g, ea, st);
+    case EPI_PARTIAL: return launch_gemm_w4_epi<EPI_PARTIAL>(W, X, x_plane, g, ea, st);
+    default: return hipErrorInvalidValue;  // the LM head keeps bf16 weights
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Block attention, bf16, head_dim 128, over the paged cache.
 // The unit of work is a 64-key page (one KV page of head g) against a query
 // tile of 32 columns; the query columns of KV head g are (q head of the

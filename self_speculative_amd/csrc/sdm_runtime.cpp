@@ -58,6 +58,13 @@ sdm_status check_config(const sdm_config* c) {
   } else {
     return fail(SDM_ERR_UNSUPPORTED, "unknown dtype %d", c->dtype);
   }
+  if (c->weight_format == SDM_WEIGHTS_INT4) {
+    if (c->dtype != SDM_BF16) return fail(SDM_ERR_UNSUPPORTED, "4-bit weights need a bf16 model");
+    if (c->d_model % kW4Group || c->ffn_dim % kW4Group)
+      return fail(SDM_ERR_UNSUPPORTED, "4-bit weights need d_model and ffn_dim multiples of %d", kW4Group);
+  } else if (c->weight_format != SDM_WEIGHTS_BF16) {
+    return fail(SDM_ERR_UNSUPPORTED, "unknown weight format %d", c->weight_format);
+  }
   return SDM_OK;
 }
 
@@ -65,6 +72,7 @@ struct Dims {
   int L, d, Hq, Hkv, hd, F, V, G, qkv, qd;
   int R, R32, max_pages, max_splits, max_slots, nq_cap;
   bool bf16;
+  bool w4;  // decoder matrices are 4-bit
   int64_t elt;
   // bf16 path: elements from the hi plane to the lo plane of each activation buffer
   int64_t xn_plane, q_plane, attn_plane, h_plane;
@@ -81,6 +89,7 @@ Dims dims_of(const sdm_config* c) {
   D.max_slots = std::min(c->max_seqs, kMaxSlots);
   D.nq_cap = D.G * D.R + 32 * D.max_slots;
   D.bf16 = c->dtype == SDM_BF16;
+  D.w4 = D.bf16 && c->weight_format == SDM_WEIGHTS_INT4;
   D.elt = D.bf16 ? 2 : 4;
   D.planes = D.bf16 ? 2 : 1;
   D.xn_plane = (int64_t)D.R32 * D.d;
@@ -116,7 +125,9 @@ Layout layout_of(const sdm_config* c) {
   Lo.ybuf = take((int64_t)D.R * ycols * 4);
   // split-K partials of the residual-stream projections (O and down)
   int smax = 1;
-  if (D.bf16)
+  if (D.w4)
+    smax = std::max(gemm_config_w4(EPI_PARTIAL, D.d, D.qd, D.R).S, gemm_config_w4(EPI_PARTIAL, D.d, D.F, D.R).S);
+  else if (D.bf16)
     smax = std::max(gemm_config(EPI_PARTIAL, D.d, D.qd, D.R).S, gemm_config(EPI_PARTIAL, D.d, D.F, D.R).S);
   Lo.part = take(D.bf16 ? (int64_t)smax * D.R * D.d * 4 : 0);
   Lo.opart = take(D.bf16 ? (int64_t)D.Hkv * D.max_splits * D.hd * D.nq_cap * 4 : 0);
@@ -254,6 +265,18 @@ KvView kv_view(const sdm_model* m, int layer) {
   return kv;
 }
 
+// The decoder's weight GEMMs (QKV, O, gate/up, down): bf16 or 4-bit weights.
+GemmShape decoder_gemm_shape(const Dims& D, int epi, int N, int K, int M) {
+  return D.w4 ? gemm_config_w4(epi, N, K, M) : gemm_config(epi, N, K, M);
+}
+
+hipError_t decoder_gemm(const Dims& D, int epi, const void* W, const uint16_t* X, int64_t x_plane, int N, int K, int M,
+                        const EpiArgs& ea, hipStream_t st) {
+  const GemmShape g = decoder_gemm_shape(D, epi, N, K, M);
+  if (D.w4) return launch_gemm_w4(epi, (const uint8_t*)W, X, x_plane, g, ea, st);
+  return launch_gemm_bf16(epi, (const uint16_t*)W, X, x_plane, g, ea, st);
+}
+
 struct TokenInput {
   const int* tokens = nullptr;  // [M] (TOK_PLAIN)
   int src = TOK_PLAIN;
@@ -312,9 +335,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
     nparts = 0;
     if (D.bf16) {
       { TimedScope ts(m, SDM_K_QKV);
-      HIP_TRY(launch_gemm_bf16(EPI_QKV, (const uint16_t*)m->w_qkv[l], (const uint16_t*)xn, D.xn_plane,
-                               gemm_config(EPI_QKV, D.qkv, D.d, M),
-                               ea, st),
+      HIP_TRY(decoder_gemm(D, EPI_QKV, m->w_qkv[l], (const uint16_t*)xn, D.xn_plane, D.qkv, D.d, M, ea, st),
               "qkv gemm"); }
       AttnArgs aa{};
       aa.q = ea.q_out;
@@ -340,23 +361,19 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       { TimedScope ts(m, SDM_K_ATTN_COMBINE);
         HIP_TRY(launch_attn_combine_bf16(aa, st), "attention combine"); }
       { TimedScope ts(m, SDM_K_O);
-        const GemmShape go = gemm_config(EPI_PARTIAL, D.d, D.qd, M);
-        nparts = go.S;
-        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_o[l], aa.out, D.attn_plane, go, ea, st),
-                "o gemm"); }
+        nparts = decoder_gemm_shape(D, EPI_PARTIAL, D.d, D.qd, M).S;
+        HIP_TRY(decoder_gemm(D, EPI_PARTIAL, m->w_o[l], aa.out, D.attn_plane, D.d, D.qd, M, ea, st), "o gemm"); }
       { TimedScope ts(m, SDM_K_NORM);
         HIP_TRY(launch_rmsnorm(m->cfg.dtype, x, ea.part, nparts, ea.part_stride, m->ffn_norm[l], eps, M, D.d, 0, xn,
                                D.xn_plane, st),
                 "rmsnorm"); }
       nparts = 0;
       { TimedScope ts(m, SDM_K_GATE_UP);
-        HIP_TRY(launch_gemm_bf16(EPI_SWIGLU, (const uint16_t*)m->w_gu[l], (const uint16_t*)xn, D.xn_plane,
-                                 gemm_config(EPI_SWIGLU, 2 * D.F, D.d, M), ea, st),
+        HIP_TRY(decoder_gemm(D, EPI_SWIGLU, m->w_gu[l], (const uint16_t*)xn, D.xn_plane, 2 * D.F, D.d, M, ea, st),
                 "gate/up gemm"); }
       { TimedScope ts(m, SDM_K_DOWN);
-        const GemmShape gd = gemm_config(EPI_PARTIAL, D.d, D.F, M);
-        nparts = gd.S;
-        HIP_TRY(launch_gemm_bf16(EPI_PARTIAL, (const uint16_t*)m->w_down[l], ea.h_out, D.h_plane, gd, ea, st),
+        nparts = decoder_gemm_shape(D, EPI_PARTIAL, D.d, D.F, M).S;
+        HIP_TRY(decoder_gemm(D, EPI_PARTIAL, m->w_down[l], ea.h_out, D.h_plane, D.d, D.F, M, ea, st),
                 "down gemm"); }
     } else {
       float* y = m->at<float>(m->lo.ybuf);
@@ -485,6 +502,37 @@ sdm_status sdm_pack_matrix(const sdm_config* cfg, int32_t kind, const void* d_sr
     if (kind == SDM_PACK_QKV && rows % cfg->head_dim) return fail(SDM_ERR_ARG, "qkv rows not a multiple of head_dim");
   }
   hipError_t e = launch_pack(cfg->dtype, kind, d_src, d_src2, d_dst, rows, cols, cfg->head_dim, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(SDM_ERR_DEVICE, "pack: %s", hipGetErrorString(e));
+  return SDM_OK;
+}
+
+size_t sdm_packed_bytes_int4(const sdm_config* cfg, int64_t rows, int64_t cols) {
+  if (check_config(cfg) != SDM_OK || cfg->dtype != SDM_BF16 || rows < 1 || cols < 1 || rows % 32 ||
+      cols % kW4Group)
+    return 0;
+  return (size_t)w4_packed_bytes(rows, cols);
+}
+
+sdm_status sdm_pack_matrix_int4(const sdm_config* cfg, int32_t kind, const void* d_codes, const void* d_scales,
+                                const void* d_codes2, const void* d_scales2, void* d_dst, int64_t rows, int64_t cols,
+                                void* hip_stream) {
+  sdm_status s = check_config(cfg);
+  if (s != SDM_OK) return s;
+  if (cfg->dtype != SDM_BF16) return fail(SDM_ERR_UNSUPPORTED, "4-bit weights need a bf16 config");
+  if (kind < SDM_PACK_PLAIN || kind > SDM_PACK_GATE_UP) return fail(SDM_ERR_ARG, "unknown pack kind %d", kind);
+  if (!d_codes || !d_scales || !d_dst || (kind == SDM_PACK_GATE_UP && (!d_codes2 || !d_scales2)))
+    return fail(SDM_ERR_ARG, "null pointer");
+  if (rows < 1 || cols < 1) return fail(SDM_ERR_ARG, "empty matrix");
+  if (cols % kW4Group) return fail(SDM_ERR_UNSUPPORTED, "4-bit packing needs cols %% %d == 0", kW4Group);
+  if (kind == SDM_PACK_GATE_UP ? rows % 16 : rows % 32)
+    return fail(SDM_ERR_UNSUPPORTED, "4-bit packing needs rows %% 32 == 0 (%% 16 for gate/up)");
+  if (kind == SDM_PACK_QKV && rows % cfg->head_dim) return fail(SDM_ERR_ARG, "qkv rows not a multiple of head_dim");
+  auto misaligned = [](const void* p) { return p && ((uintptr_t)p & 3); };
+  if (misaligned(d_codes) || misaligned(d_codes2) || misaligned(d_dst) || misaligned(d_scales) ||
+      misaligned(d_scales2))
+    return fail(SDM_ERR_ARG, "4-bit packing needs 4-byte aligned buffers");
+  hipError_t e = launch_pack_w4(kind, d_codes, d_scales, d_codes2, d_scales2, d_dst, rows, cols, cfg->head_dim,
+                                (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(SDM_ERR_DEVICE, "pack: %s", hipGetErrorString(e));
   return SDM_OK;
 }

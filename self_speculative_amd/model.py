@@ -24,17 +24,19 @@ def _dev_tensor(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
 
 
-def make_config(shape, max_seqs=1, max_block=32, max_context=4096, max_rows=32) -> L.SdmConfig:
+def make_config(shape, max_seqs=1, max_block=32, max_context=4096, max_rows=32,
+                weight_format=L.SDM_WEIGHTS_BF16) -> L.SdmConfig:
     return L.SdmConfig(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                        shape.ffn_dim, shape.vocab, shape.mask_id, shape.rope_base, shape.rms_eps,
                        L.SDM_BF16 if shape.dtype == "bf16" else L.SDM_F32, 64, max_seqs, max_block, max_context,
-                       max_rows)
+                       max_rows, weight_format)
 
 
 class Model:
     """A decoder on one GPU.  ``weights`` is a dict as produced by
-    ``workloads.make_weights`` (host numpy arrays); they are uploaded and
-    packed into the library's layout once."""
+    ``workloads.make_weights`` or ``workloads.make_w4_weights`` (host numpy
+    arrays; 4-bit decoder matrices are recognised by their ``.codes``
+    entries); they are uploaded and packed into the library's layout once."""
 
     def __init__(self, shape, weights: Dict[str, np.ndarray], *, max_seqs: int = 1, max_block: int = 32,
                  max_context: int = 4096, max_rows: int = 32, n_pages: Optional[int] = None,
@@ -42,7 +44,9 @@ class Model:
         self.lib = L.lib()
         self.shape = shape
         self.device = torch.device(device)
-        self.cfg = make_config(shape, max_seqs, max_block, max_context, max_rows)
+        self.w4 = "layers.0.w_qkv.codes" in weights
+        self.cfg = make_config(shape, max_seqs, max_block, max_context, max_rows,
+                               L.SDM_WEIGHTS_INT4 if self.w4 else L.SDM_WEIGHTS_BF16)
         self.stream = torch.cuda.current_stream(self.device)
         st = c_void_p(self.stream.cuda_stream)
         cfgp = ctypes.byref(self.cfg)
@@ -52,6 +56,27 @@ class Model:
             nbytes = self.lib.sdm_packed_bytes(cfgp, rows * (2 if kind == L.SDM_PACK_GATE_UP else 1), cols)
             dst = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
             L.check(self.lib.sdm_pack_matrix(cfgp, kind, L.ptr(src), L.ptr(src2), L.ptr(dst), rows, cols, st))
+            self._keep.append(dst)
+            return dst
+
+        def packed_int4(kind, rows, cols, name, name2=None):
+            """Upload <name>.codes / .scales (and name2's for gate/up), pack them."""
+            srcs = []
+            for n in (name, name2):
+                if n is None:
+                    srcs += [None, None]
+                    continue
+                c = torch.from_numpy(np.ascontiguousarray(weights[n + ".codes"])).to(self.device)
+                sc = torch.from_numpy(np.ascontiguousarray(weights[n + ".scales"]).view(np.int16)).to(self.device)
+                srcs += [c, sc]
+                if free_host:
+                    weights.pop(n + ".codes")
+                    weights.pop(n + ".scales")
+            nbytes = self.lib.sdm_packed_bytes_int4(cfgp, rows * (2 if kind == L.SDM_PACK_GATE_UP else 1), cols)
+            if nbytes == 0:
+                raise L.SdmError(L.SDM_ERR_UNSUPPORTED, f"4-bit matrix {name} [{rows}, {cols}]")
+            dst = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            L.check(self.lib.sdm_pack_matrix_int4(cfgp, kind, *[L.ptr(x) for x in srcs], L.ptr(dst), rows, cols, st))
             self._keep.append(dst)
             return dst
 
@@ -79,6 +104,13 @@ class Model:
             p = f"layers.{l}."
             per["attn_norm"].append(plain(p + "attn_norm"))
             per["ffn_norm"].append(plain(p + "ffn_norm"))
+            if self.w4:
+                per["w_qkv"].append(packed_int4(L.SDM_PACK_QKV, s.qkv_dim, s.d_model, p + "w_qkv"))
+                per["w_o"].append(packed_int4(L.SDM_PACK_PLAIN, s.d_model, s.q_dim, p + "w_o"))
+                per["w_gate_up"].append(packed_int4(L.SDM_PACK_GATE_UP, s.ffn_dim, s.d_model, p + "w_gate",
+                                                    p + "w_up"))
+                per["w_down"].append(packed_int4(L.SDM_PACK_PLAIN, s.d_model, s.ffn_dim, p + "w_down"))
+                continue
             t = upload(p + "w_qkv")
             per["w_qkv"].append(packed(L.SDM_PACK_QKV, s.qkv_dim, s.d_model, t))
             t = upload(p + "w_o")

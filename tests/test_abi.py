@@ -74,6 +74,34 @@ def test_calls_reject_bad_arguments_without_a_device(lib):
     assert lib.sdm_attn_pool_bytes(8, 128, 10) == 10 * 2 * 8 * 64 * 128 * 2
 
 
+def test_int4_weight_format_config_and_sizes(lib):
+    from self_speculative_amd import _lib as L
+    c = _cfg(weight_format=L.SDM_WEIGHTS_INT4)
+    assert lib.sdm_workspace_bytes(ctypes.byref(c)) > 0
+    # codes: 4096 x 4096 / 2 bytes; scales: 4096 rows x 32 groups x 2 bytes
+    assert lib.sdm_packed_bytes_int4(ctypes.byref(c), 4096, 4096) == 4096 * 2048 + 4096 * 32 * 2
+    # 6144 x 4096 QKV, 2 x 12288 gate/up rows
+    assert lib.sdm_packed_bytes_int4(ctypes.byref(c), 6144, 4096) == 6144 * 2048 + 6144 * 32 * 2
+    assert lib.sdm_packed_bytes_int4(ctypes.byref(c), 24576, 4096) == 24576 * 2048 + 24576 * 32 * 2
+    assert lib.sdm_packed_bytes_int4(ctypes.byref(c), 4096, 4000) == 0
+    assert lib.sdm_packed_bytes_int4(ctypes.byref(c), 4016, 4096) == 0
+    for bad in (dict(weight_format=2), dict(weight_format=L.SDM_WEIGHTS_INT4, dtype=L.SDM_F32, head_dim=64),
+                dict(weight_format=L.SDM_WEIGHTS_INT4, d_model=4096 + 32)):
+        b = _cfg(**bad)
+        assert lib.sdm_workspace_bytes(ctypes.byref(b)) == 0, bad
+        assert lib.sdm_last_error().decode()
+    # packing arguments are checked before any HIP call
+    pk = lib.sdm_pack_matrix_int4
+    assert pk(ctypes.byref(c), 9, 4, 4, None, None, 4, 32, 128, None) == L.SDM_ERR_ARG
+    assert pk(ctypes.byref(c), 0, None, 4, None, None, 4, 32, 128, None) == L.SDM_ERR_ARG
+    assert pk(ctypes.byref(c), 2, 4, 4, None, 4, 4, 32, 128, None) == L.SDM_ERR_ARG
+    assert pk(ctypes.byref(c), 0, 4, 4, None, None, 4, 32, 100, None) == L.SDM_ERR_UNSUPPORTED
+    assert pk(ctypes.byref(c), 0, 4, 4, None, None, 4, 31, 128, None) == L.SDM_ERR_UNSUPPORTED
+    assert pk(ctypes.byref(c), 0, 6, 4, None, None, 4, 32, 128, None) == L.SDM_ERR_ARG
+    f32 = _cfg(dtype=L.SDM_F32, head_dim=64, n_q_heads=32, n_kv_heads=8)
+    assert pk(ctypes.byref(f32), 0, 4, 4, None, None, 4, 32, 128, None) == L.SDM_ERR_UNSUPPORTED
+
+
 def test_product_path_does_not_import_the_oracle():
     """The package's sources never reference the oracle (it is test-only)."""
     pkg = os.path.join(ROOT, "self_speculative_amd")
