@@ -33,22 +33,31 @@ def layer_weight_bytes(s) -> dict:
     return {"qkv": s.qkv_dim * d * 2, "o": d * s.q_dim * 2, "gate_up": 2 * F * d * 2, "down": d * F * 2}
 
 
-def forward_bytes(s, n: int, T: int) -> int:
+def forward_bytes(s, n: int, T: int, w4: bool = False) -> int:
     """Algorithmic HBM bytes of one T-row forward at committed length n:
     every weight once, the KV prefix read, the block's K/V written, the
     gathered embedding rows."""
-    w = sum(layer_weight_bytes(s).values()) * s.n_layers + s.vocab * s.d_model * 2
+    lw = layer_weight_bytes_w4(s) if w4 else layer_weight_bytes(s)
+    w = sum(lw.values()) * s.n_layers + s.vocab * s.d_model * 2
     kv_tok = s.n_layers * 2 * s.n_kv_heads * s.head_dim * 2
     return w + (n + T) * kv_tok + T * kv_tok + T * s.d_model * 2
 
 
-def kernel_bytes(s, cls: str, M: int) -> int:
+def layer_weight_bytes_w4(s) -> dict:
+    """4-bit decoder matrices: half a byte per weight plus a bf16 scale per
+    128 inputs."""
+    d, F = s.d_model, s.ffn_dim
+    nk = {"qkv": (s.qkv_dim, d), "o": (d, s.q_dim), "gate_up": (2 * F, d), "down": (d, F)}
+    return {k: n * k_ // 2 + n * (k_ // 128) * 2 for k, (n, k_) in nk.items()}
+
+
+def kernel_bytes(s, cls: str, M: int, w4: bool = False) -> int:
     """Algorithmic bytes of one launch of a GEMM class at M rows: weights +
     activations in + activations out.  Activations handed between kernels are
     two bf16 planes (4 bytes an element); k/v go to the cache as bf16; the O
     and down projections' result is one fp32 residual update per element."""
     d, F = s.d_model, s.ffn_dim
-    lw = layer_weight_bytes(s)
+    lw = layer_weight_bytes_w4(s) if w4 else layer_weight_bytes(s)
     io = {"qkv": M * d * 4 + M * s.q_dim * 4 + M * 2 * s.kv_dim * 2,
           "o": M * s.q_dim * 4 + M * d * 4,
           "gate_up": M * d * 4 + M * F * 4,
@@ -87,6 +96,8 @@ def main() -> int:
                     help="run only the standalone attention op measurement (for profilers) and print it")
     ap.add_argument("--batch14b", action="store_true",
                     help="also measure the 14B-shaped 16-sequence batched diffusion block (draws ~30 GB of weights)")
+    ap.add_argument("--no-w4", action="store_true", help="skip the 4-bit weight (w4a16) pass of the extras")
+    ap.add_argument("--w4-only", action="store_true", help="only the 4-bit weight (w4a16) pass (for profilers)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -111,6 +122,12 @@ def main() -> int:
         return 0
     s = W.SHAPES["8b"]
     B = 32
+    if args.w4_only:
+        sched = W.forced_accept_schedule(8192, B, seed=0)
+        K = args.steps or 115
+        print(json.dumps({"w4a16": w4a16_bench(log, s, W.prompt_ids(s, args.prompt, seed=0), sched, K, args.warmup,
+                                                4096)}), flush=True)
+        return 0
     t0 = time.time()
     weights = W.make_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
     log(f"weights drawn in {time.time() - t0:.1f}s")
@@ -292,6 +309,13 @@ def main() -> int:
                                             "tpf": round(tokens / (2 * K), 3)},
                         "prefill_1024_ms": round(t_pf * 1e3, 2)}
 
+    if not args.no_extras and not args.no_w4:
+        model.close()
+        del model
+        torch.cuda.empty_cache()
+        model = None
+        out["w4a16"] = w4a16_bench(log, s, prompt, sched, K, args.warmup, max_ctx)
+
     if args.calib_copy:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -304,13 +328,101 @@ def main() -> int:
         del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(s, weights, prompt, tokens / K, log)
-    model.close()
+    if model is not None:
+        model.close()
     if args.batch14b:
         del weights
         torch.cuda.empty_cache()
         out["batch_14b"] = batch14b_bench(log)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx) -> dict:
+    """The headline workload with the decoder's matrices in 4 bits (group-wise
+    int4 + bf16 scales; embedding and LM head bf16): forced self-spec rate,
+    per-class kernel times and the 4-bit gate/up GEMM against HBM."""
+    import torch
+
+    import workloads as W
+    from self_speculative_amd.decode import SelfSpecRun, prefill
+    from self_speculative_amd.model import Model
+    B = 32
+    t0 = time.time()
+    w = W.make_w4_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
+    log(f"w4a16: weights drawn in {time.time() - t0:.1f}s")
+    model = Model(s, w, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=128, free_host=True)
+    del w
+    torch.cuda.synchronize()
+    log(f"w4a16: model uploaded + packed ({model.weight_bytes / 1e9:.2f} GB)")
+    dev = model.device
+
+    def run_cycles(seq, n_cyc, sched_vals, first):
+        run = SelfSpecRun(model, B, seq)
+        blocks = torch.empty((n_cyc, B), dtype=torch.int32, device=dev)
+        ars = torch.empty((n_cyc, B), dtype=torch.int32, device=dev)
+        anchor = first.data_ptr()
+        Ls = []
+        for c in range(n_cyc):
+            run.block, run.ar = blocks[c], ars[c]
+            L = run.cycle(anchor, int(sched_vals[c]))
+            Ls.append(L)
+            anchor = ars[c].data_ptr() + 4 * (L - 1)
+        return Ls
+
+    first = prefill(model, 1, prompt)
+    run_cycles(1, warmup, W.forced_accept_schedule(warmup, B, seed=1), first)
+    torch.cuda.synchronize()
+    model.seq_reset(1)
+    first = prefill(model, 0, prompt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    Ls = run_cycles(0, K, sched[:K], first)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tokens = int(sum(Ls))
+    log(f"w4a16 self-spec forced: {K} cycles, {tokens} tokens in {wall * 1e3:.1f} ms -> {tokens / wall:.1f} tok/s")
+    # per-class timing on sequence 1
+    model.seq_reset(0)
+    first = prefill(model, 1, prompt)
+    classes = ["gate_up", "down", "qkv", "o", "forward"]
+    n_cyc = 6
+    ex = W.forced_accept_schedule(n_cyc * len(classes), B, seed=2)
+    per, ns, pos = {}, [], 0
+    run = SelfSpecRun(model, B, 1)
+    rb = torch.empty((n_cyc * len(classes), B), dtype=torch.int32, device=dev)
+    ra = torch.empty((n_cyc * len(classes), B), dtype=torch.int32, device=dev)
+    anchor = first.data_ptr()
+    for cls in classes:
+        torch.cuda.synchronize()
+        model.timing_start(cls, 4096)
+        for c in range(n_cyc):
+            run.block, run.ar = rb[pos], ra[pos]
+            ns.append(model.seq_length(1))
+            L = run.cycle(anchor, int(ex[pos]))
+            anchor = ra[pos].data_ptr() + 4 * (L - 1)
+            pos += 1
+        n, tot_ms, mn, mx = model.timing_stop()
+        per[cls] = {"launches": n, "avg_us": round(tot_ms / max(1, n) * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                    "max_us": round(mx * 1e3, 2)}
+        if cls != "forward":
+            b = kernel_bytes(s, cls, B, w4=True)
+            per[cls]["bytes"] = b
+            per[cls]["GBps"] = round(b / (per[cls]["avg_us"] * 1e-6) / 1e9, 1)
+        log(f"w4a16 {cls:>8}: {n} launches, avg {per[cls]['avg_us']} us")
+    model.close()
+    gu = per["gate_up"]
+    f_us = per["forward"]["avg_us"]
+    fb = forward_bytes(s, int(statistics.mean(ns[-n_cyc:])), B, w4=True)
+    ach = gu["bytes"] / (gu["avg_us"] * 1e-6) / 1e9
+    return {"workload": "the headline workload (8B shape, prompt 1024, block 32, forced accept U{1..32} seed 0) "
+                        "with QKV, O, gate/up and down as group-wise int4 + bf16 scales (group 128)",
+            "tok_per_s": round(tokens / wall, 1), "ms_per_step": round(wall * 1e3 / K, 4), "steps": K,
+            "kernels": per,
+            "forward": {"avg_us": f_us, "algorithmic_bytes": fb, "hbm_frac": round(fb / (f_us * 1e-6) / 8e12, 4)},
+            "roofline_gate_up": {"bound": "hbm", "kernel": "k_gemm_w4<EPI_SWIGLU>, M=32", "achieved": round(ach, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                 "bytes_per_launch": gu["bytes"], "avg_launch_us": gu["avg_us"]}}
 
 
 def _pct(vals):

@@ -158,11 +158,17 @@ constexpr int kW4GroupBlocks = kW4Group / 16;  // k-blocks per scale group
 inline int64_t w4_scale_offset(int64_t N, int64_t K) { return ((N * K / 2) + 255) / 256 * 256; }
 inline int64_t w4_packed_bytes(int64_t N, int64_t K) { return w4_scale_offset(N, K) + N * (K / kW4Group) * 2; }
 
-// Launch configuration of a 4-bit matrix: gemm_config's split and tile choice,
-// with every split a whole number of scale groups and at most four
-// accumulator tiles per wave (MT * TP <= 4; the wave keeps a running total and
-// the current group's sum of each).  As for bf16, nothing depends on the
-// number of rows except which workgroup computes which tile.
+// Launch configuration of a 4-bit matrix.  kW4Waves waves per workgroup take
+// the scale groups of its K range round robin.  Split-K (EPI_PARTIAL only):
+// the smallest S with every split a whole number of groups (at least one per
+// wave) that gives 2 * kGemmTargetGroups (split, tile) pairs, so that
+// workgroups of two weight tiles still cover the chip; else the largest valid
+// S.  TP: the most weight tiles per workgroup (MT * TP <= 4: a wave holds a
+// running total and the current group's sum of each tile) that keep
+// kGemmTargetGroups workgroups.  S and the waves depend on the matrix shape
+// only, never on the number of rows, so every row's result is independent of
+// the batch.
+constexpr int kW4Waves = 8;
 inline GemmShape gemm_config_w4(int epi, int N, int K, int rows) {
   GemmShape g;
   g.NT = N / 32;
@@ -171,17 +177,23 @@ inline GemmShape gemm_config_w4(int epi, int N, int K, int rows) {
   g.S = 1;
   if (epi == EPI_PARTIAL) {
     auto ok = [&](int s) {
-      return s <= kMaxSplitK && g.KB % s == 0 && (g.KB / s) % kW4GroupBlocks == 0 && g.KB / s >= 32;
+      return g.KB % (s * kW4GroupBlocks) == 0 && g.KB / (s * kW4GroupBlocks) >= kW4Waves;
     };
-    while (g.NT * g.S < kGemmTargetGroups && ok(2 * g.S)) g.S *= 2;
-    while (ok(2 * g.S) && g.KB / (2 * g.S) >= 96 && g.NT * 2 * g.S <= 4 * kGemmTargetGroups) g.S *= 2;
+    int best = 1;
+    for (int s = 2; s <= kMaxSplitK; s *= 2)
+      if (ok(s)) best = s;
+    for (int s = 1; s <= kMaxSplitK; s *= 2)
+      if (ok(s) && g.NT * s >= 2 * kGemmTargetGroups) {
+        best = s;
+        break;
+      }
+    g.S = best;
   }
-  g.WAVES = 4;
+  g.WAVES = kW4Waves;
   g.TP = 1;
   const int mt = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
   const int mgroups = (g.MTILES + mt - 1) / mt;
-  const int tmax = 4 / mt;
-  for (int t = tmax; t > 1; --t)
+  for (int t = 4 / mt; t > 1; --t)
     if (g.NT % t == 0 && (g.NT / t) * g.S * mgroups >= kGemmTargetGroups) {
       g.TP = t;
       break;

@@ -650,15 +650,21 @@ hipError_t launch_pack_w4(int kind, const void* codes, const void* scales, const
 }
 
 // The 8 codes of one k-block of a lane (nibble e at bits 4e) as the bf16 MFMA
-// operand: 4 words, each two bf16 integers (element 2j low, 2j + 1 high).
-// A code converts to fp32 exactly, and its bf16 bits are the top half.
+// operand, times 16: 4 words, each two bf16 integers 16 * q (element 2j low,
+// 2j + 1 high).  Moving a nibble to the top of a byte makes the byte the
+// signed integer 16 * q, which converts to fp32 exactly (a byte-select
+// convert); its bf16 bits are the top half.  The factor 16 is a power of two:
+// every group sum, and every running total built from them, is exactly 16
+// times the unscaled one (no rounding differs), and the kernel divides the
+// totals by 16 once at the end.
 __device__ __forceinline__ u32x4 w4_operand(uint32_t w) {
+  const uint32_t even = (w << 4) & 0xF0F0F0F0u, odd = w & 0xF0F0F0F0u;  // codes 2j / 2j + 1 in byte j
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int q0 = (int)(w << (28 - 8 * j)) >> 28;
-    const int q1 = (int)(w << (24 - 8 * j)) >> 28;
-    r[j] = __builtin_amdgcn_perm(__float_as_uint((float)q1), __float_as_uint((float)q0), 0x07060302u);
+    const float f0 = (float)(int8_t)(even >> (8 * j));
+    const float f1 = (float)(int8_t)(odd >> (8 * j));
+    r[j] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   }
   return r;
 }
@@ -669,15 +675,17 @@ __device__ __forceinline__ float w4_scale(const u32x4 (&s)[2], int r) {
   return __uint_as_float((r & 1) ? (u & 0xffff0000u) : (u << 16));
 }
 
-// Grid (NT / TP, S, ceil(MTILES / MT)), 4 waves.  The workgroup's K range
-// goes to the waves by scale group, round robin; a wave adds its groups in
-// increasing order and the waves' totals meet in LDS in wave order, as in
-// k_gemm_bf16, so a row's result does not depend on the batch it is in.
+// Grid (NT / TP, S, ceil(MTILES / MT)), kW4Waves waves (two per SIMD, so
+// one wave's code conversion overlaps the other's loads and products).  The
+// workgroup's K range goes to the waves by scale group, round robin; a wave
+// adds its groups in increasing order and the waves' totals meet in LDS in
+// wave order, so a row's result does not depend on the batch it is in.
 template <int EPI, int MT, int TP>
-__global__ __launch_bounds__(256) void k_gemm_w4(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Ws,
-                                                 const uint16_t* __restrict__ X, int64_t x_plane, GemmShape g,
-                                                 EpiArgs ea) {
-  constexpr int WAVES = 4, GB = kW4GroupBlocks;
+__global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __restrict__ Wc,
+                                                           const uint16_t* __restrict__ Ws,
+                                                           const uint16_t* __restrict__ X, int64_t x_plane,
+                                                           GemmShape g, EpiArgs ea) {
+  constexpr int WAVES = kW4Waves, GB = kW4GroupBlocks;
   static_assert(MT * TP <= 4, "a wave holds a total and a group sum per tile");
   const int nt0 = blockIdx.x * TP, sk = blockIdx.y, mg = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
@@ -751,51 +759,29 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const uint8_t* __restrict__ Wc,
       }
   }
 
-  if constexpr (MT == 1) {
-    __shared__ float red[TP][WAVES][16][64];
+  // The MT x TP output tiles (activation tile major, at most 4) go through
+  // LDS; wave q sums tile q over the waves in order (after undoing
+  // w4_operand's factor 16, exactly) and finishes it.
+  __shared__ float red[4][WAVES][16][64];
+  const int ntile = mcount * TP;
 #pragma unroll
-    for (int t = 0; t < TP; ++t)
+  for (int q = 0; q < MT * TP; ++q)
+    if (q < ntile) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[t][wave][r][lane] = tot[0][t][r];
-    __syncthreads();
-    if (wave < TP) {
-      float c[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = red[wave][0][r][lane];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
-        c[r] = v;
-      }
-      gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
+      for (int r = 0; r < 16; ++r) red[q][wave][r][lane] = tot[q / TP][q % TP][r] * 0.0625f;
     }
-  } else {
-    __shared__ float red[WAVES][WAVES][16][64];
-    const int ntile = mcount * TP;
+  __syncthreads();
+  if (wave < ntile) {
+    float c[16];
 #pragma unroll
-    for (int q0 = 0; q0 < MT * TP; q0 += WAVES) {
-      if (q0 >= ntile) break;
-      if (q0 > 0) __syncthreads();
+    for (int r = 0; r < 16; ++r) {
+      float v = red[wave][0][r][lane];
 #pragma unroll
-      for (int qs = 0; qs < WAVES; ++qs)
-        if (q0 + qs < MT * TP && q0 + qs < ntile) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) red[qs][wave][r][lane] = tot[(q0 + qs) / TP][(q0 + qs) % TP][r];
-        }
-      __syncthreads();
-      const int q = q0 + wave;
-      if (q < ntile) {
-        float c[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = red[wave][0][r][lane];
-#pragma unroll
-          for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
-          c[r] = v;
-        }
-        gemm_epilogue<EPI, false>(c, nt0 + q % TP, mt0 + q / TP, lane, ea, pre);
-      }
+      for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
+      c[r] = v;
     }
+    if constexpr (MT == 1) gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
+    else gemm_epilogue<EPI, false>(c, nt0 + wave % TP, mt0 + wave / TP, lane, ea, pre);
   }
 }
 
@@ -804,9 +790,9 @@ static hipError_t launch_gemm_w4_epi(const uint8_t* W, const uint16_t* X, int64_
                                      const EpiArgs& ea, hipStream_t st) {
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
   const int TP = g.TP;
-  if (g.WAVES != 4 || MT * TP > 4 || g.NT % TP || g.KB % (g.S * kW4GroupBlocks)) return hipErrorInvalidValue;
+  if (g.WAVES != kW4Waves || MT * TP > 4 || g.NT % TP || g.KB % (g.S * kW4GroupBlocks)) return hipErrorInvalidValue;
   const uint16_t* Ws = (const uint16_t*)(W + w4_scale_offset((int64_t)g.NT * 32, (int64_t)g.KB * 16));
-  const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(256);
+  const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(64 * kW4Waves);
   if (MT == 1) {
     if (TP == 1) SDM_LAUNCH((k_gemm_w4<EPI, 1, 1>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
     else if (TP == 2) SDM_LAUNCH((k_gemm_w4<EPI, 1, 2>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
