@@ -16,4 +16,4 @@ from .model import (BIDIR, CAUSAL, INT4_GROUP, KVCache, OracleModel, apply_rope,
                     bf16_round, decode_bf16_bits, dequant_int4, int4_codes, rms_normalize, rope_tables, select_rows,
                     silu, visible)
 from .modes import (GenResult, OracleSession, RowSel, accept_length, generate_ar, generate_diffusion,
-                    generate_diffusion_batch, generate_selfspec, unmask_rule)
+                    generate_diffusion_batch, generate_selfspec, revise_rule, unmask_rule)

@@ -16,6 +16,8 @@ modes as the pages state them:
   round unmasks the masked positions whose confidence clears a threshold,
   and always at least the most confident one; a step budget caps the rounds
   (aimodeling English text: fewer refinement steps cut the inference budget).
+  Optionally a round also revises positions already written (the pages: the
+  model can go back and modify generated content; the rule is a reading).
 * Self-speculation: diffusion drafts a block in parallel and AR verifies it in
   one forward (ai-feeds item 3; hotpaper abstract point (2)).  The draft is
   kept up to the first token the AR argmax disagrees with; the AR token at
@@ -69,6 +71,21 @@ def unmask_rule(block: np.ndarray, tok: np.ndarray, conf: np.ndarray, tau: float
         U = np.union1d(masked[c > tau], [best]).astype(np.int64)
     block[U] = tok[U]
     return block, U, int(masked.size - U.size)
+
+
+def revise_rule(block: np.ndarray, tok: np.ndarray, conf: np.ndarray, tau_revise: float, mask_id: int):
+    """Revision of positions already written (the pages: in diffusion mode the
+    model can go back and modify content it has already generated --
+    fintech-frontier-insights, three generation modes, diffusion bullet; the
+    aimodeling text.  The rule is a reading: the pages give none).
+
+    R = {i : block_i is not MASK, tok_i != block_i, conf_i > tau_revise}; the
+    positions in R take tok_i.  conf <= 1, so tau_revise >= 1 revises nothing.
+    Returns (new block, R as a sorted index array)."""
+    block = np.array(block, dtype=np.int32, copy=True)
+    R = np.nonzero((block != mask_id) & (np.asarray(tok) != block) & (np.asarray(conf) > tau_revise))[0]
+    block[R] = np.asarray(tok)[R]
+    return block, R
 
 
 def accept_length(block: np.ndarray, ar_tok: np.ndarray) -> int:
@@ -149,6 +166,20 @@ class OracleSession:
         new, U, n_left = unmask_rule(np.asarray(block), sel.tok, sel.conf, tau, force_all, self.mask_id)
         return new, U, n_left, sel
 
+    def diffuse_step_revise(self, seq: int, block: Sequence[int], tau: float, tau_revise: float, force_all: bool):
+        """A denoising step with revision: from the same forward, the masked
+        positions follow the unmask rule and the written ones the revise rule,
+        both decided on the block as it was before the step.  Returns
+        (new block, U, R, |Mk \\ U|, row selections)."""
+        c = self._cache(seq)
+        before = np.asarray(block, dtype=np.int32)
+        sel = self._sel(self.model.forward(c, before, BIDIR))
+        self.forwards += 1
+        new, U, n_left = unmask_rule(before, sel.tok, sel.conf, tau, force_all, self.mask_id)
+        revised, R = revise_rule(before, sel.tok, sel.conf, tau_revise, self.mask_id)
+        new[R] = revised[R]
+        return new, U, R, n_left, sel
+
 
 # -- generation loops -----------------------------------------------------------
 @dataclass
@@ -158,6 +189,7 @@ class GenResult:
     accept_lengths: List[int] = field(default_factory=list)
     steps_per_block: List[int] = field(default_factory=list)
     margins: List[float] = field(default_factory=list)
+    revisions: List[int] = field(default_factory=list)
 
     @property
     def tpf(self) -> float:
@@ -197,20 +229,28 @@ def generate_selfspec(model: OracleModel, prompt: Sequence[int], n_tokens: int, 
 
 
 def generate_diffusion(model: OracleModel, prompt: Sequence[int], n_tokens: int, B: int,
-                       tau: float, max_steps: Optional[int] = None, seq: int = 0) -> GenResult:
+                       tau: float, max_steps: Optional[int] = None, seq: int = 0,
+                       tau_revise: Optional[float] = None) -> GenResult:
     """Block diffusion: each block starts all-MASK; steps until none is left
-    (step ``max_steps``-1 unmasks everything); then a causal commit forward."""
+    (step ``max_steps``-1 unmasks everything); then a causal commit forward.
+    With ``tau_revise`` every step also applies the revise rule to the
+    positions already written (the steps still end when no MASK is left)."""
     sess = OracleSession(model, keep_logits=False)
     sess.prefill(seq, prompt)
     mask = model.shape.mask_id
     toks: List[int] = []
     steps: List[int] = []
+    revs: List[int] = []
     while len(toks) < n_tokens:
         blk = np.full(B, mask, dtype=np.int32)
-        s = 0
+        s = nrev = 0
         while True:
             force = max_steps is not None and s == max_steps - 1
-            blk, _, left, _ = sess.diffuse_step(seq, blk, tau, force)
+            if tau_revise is None:
+                blk, _, left, _ = sess.diffuse_step(seq, blk, tau, force)
+            else:
+                blk, _, R, left, _ = sess.diffuse_step_revise(seq, blk, tau, tau_revise, force)
+                nrev += len(R)
             s += 1
             if left == 0:
                 break
@@ -218,11 +258,14 @@ def generate_diffusion(model: OracleModel, prompt: Sequence[int], n_tokens: int,
         sess.commit_kv(seq, B)
         toks += [int(t) for t in blk]
         steps.append(s)
-    return GenResult(toks[:n_tokens], sess.forwards - 1, steps_per_block=steps)
+        revs.append(nrev)
+    return GenResult(toks[:n_tokens], sess.forwards - 1, steps_per_block=steps, revisions=revs)
 
 
 def generate_diffusion_batch(model: OracleModel, prompts: Sequence[Sequence[int]], n_tokens: int,
-                             B: int, tau: float, max_steps: Optional[int] = None):
+                             B: int, tau: float, max_steps: Optional[int] = None,
+                             tau_revise: Optional[float] = None):
     """Several sequences in lockstep per block.  In the oracle the sequences
     never interact, so this is each sequence decoded on its own."""
-    return [generate_diffusion(model, p, n_tokens, B, tau, max_steps, seq=i) for i, p in enumerate(prompts)]
+    return [generate_diffusion(model, p, n_tokens, B, tau, max_steps, seq=i, tau_revise=tau_revise)
+            for i, p in enumerate(prompts)]

@@ -178,6 +178,71 @@ def test_step_cap_forces_all():
     assert left == 0 and list(new) == list(range(6))
 
 
+# -- revision (remasking) variant of diffusion ---------------------------------------------
+def test_revise_rule_planted():
+    mask = 9
+    block = np.array([3, mask, 5, 5, 7, 1], dtype=np.int32)
+    tok = np.array([4, 2, 5, 6, 8, 0], dtype=np.int32)
+    conf = np.array([0.95, 0.99, 0.99, 0.5, 0.95, 0.9], dtype=np.float64)
+    # position 0: differs, conf 0.95 > 0.9 -> revised; 1: masked (never revised); 2: same token;
+    # 3: differs but conf 0.5; 4: differs, 0.95 -> revised; 5: differs, conf exactly tau (strict >) -> kept
+    new, R = O.revise_rule(block, tok, conf, 0.9, mask)
+    assert list(R) == [0, 4]
+    assert list(new) == [4, mask, 5, 5, 8, 1]
+    new1, R1 = O.revise_rule(block, tok, np.ones(6), 1.0, mask)     # conf <= 1: tau 1 revises nothing
+    assert len(R1) == 0 and list(new1) == list(block)
+
+
+def test_revise_rule_brute_force():
+    r = np.random.default_rng(2)
+    mask = 99
+    for _ in range(2000):
+        B = int(r.integers(1, 10))
+        block = np.where(r.random(B) < 0.4, mask, r.integers(0, 6, B)).astype(np.int32)
+        tok = r.integers(0, 6, B).astype(np.int32)                # small alphabet: many equal tokens
+        conf = np.round(r.random(B), 1)
+        tau = float(r.choice([0.0, 0.3, 0.5, 0.9, 1.0]))
+        got, R = O.revise_rule(block, tok, conf, tau, mask)
+        exp = list(block)
+        rev = []
+        for i in range(B):
+            if block[i] != mask and tok[i] != block[i] and conf[i] > tau:
+                exp[i] = tok[i]
+                rev.append(i)
+        assert list(got) == exp and list(R) == rev
+
+
+def test_diffuse_step_revise_decides_on_the_block_before_the_step(tiny, prompt):
+    """Masked positions follow the unmask rule, written ones the revise rule,
+    both from the same forward; with tau_revise >= 1 it is the plain step."""
+    sess = O.OracleSession(tiny)
+    sess.prefill(0, prompt)
+    blk = np.full(8, TINY.mask_id, dtype=np.int32)
+    blk[[1, 4, 6]] = [3, 17, 200]
+    new_p, U_p, left_p, sel_p = sess.diffuse_step(0, blk, 0.0045, False)
+    new_1, U_1, R_1, left_1, sel_1 = sess.diffuse_step_revise(0, blk, 0.0045, 1.0, False)
+    assert len(R_1) == 0 and np.array_equal(new_p, new_1) and left_p == left_1
+    np.testing.assert_array_equal(sel_p.logits, sel_1.logits)
+    new, U, R, left, sel = sess.diffuse_step_revise(0, blk, 0.0045, 0.0, False)
+    assert set(R) == {i for i in (1, 4, 6) if sel.tok[i] != blk[i]} and len(R) > 0
+    for i in range(8):
+        if blk[i] == TINY.mask_id:
+            assert new[i] == new_p[i]                          # unmask rule untouched
+        else:
+            assert new[i] == (sel.tok[i] if i in R else blk[i])
+
+
+def test_diffusion_with_revision(tiny, prompt):
+    plain = O.generate_diffusion(tiny, prompt, 24, 8, tau=0.0045)
+    off = O.generate_diffusion(tiny, prompt, 24, 8, tau=0.0045, tau_revise=1.0)
+    assert off.tokens == plain.tokens and off.revisions == [0, 0, 0]
+    on = O.generate_diffusion(tiny, prompt, 24, 8, tau=1.01, tau_revise=0.0)   # one unmask per step
+    assert sum(on.revisions) > 0 and on.steps_per_block == [8, 8, 8]
+    assert len(on.tokens) == 24 and TINY.mask_id not in on.tokens
+    for s in on.steps_per_block:
+        assert 1 <= s <= 8
+
+
 # -- I6: committed cache equals a fresh prefill -------------------------------------------
 def test_commit_equals_fresh_prefill(tiny, prompt):
     sess = O.OracleSession(tiny, keep_logits=False)
