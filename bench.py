@@ -302,6 +302,36 @@ def main() -> int:
         prefill(model, 1, prompt)
         torch.cuda.synchronize()
         t_pf = time.perf_counter() - t0
+        # block diffusion: step budget sweep (random weights never clear tau = 0.9, so a block takes exactly
+        # S bidirectional steps -- one position each, all of the rest on the last -- plus the causal commit)
+        diff = {}
+        nm = torch.empty(1, dtype=torch.int32, device=dev)
+        blk = torch.empty((1, B), dtype=torch.int32, device=dev)
+        ar = torch.empty(B, dtype=torch.int32, device=dev)
+        acc1 = torch.empty(1, dtype=torch.int32, device=dev)
+        for S, taur in [(1, None), (2, None), (4, None), (8, None), (16, None), (32, None), (8, 0.9)]:
+            model.seq_reset(1)
+            prefill(model, 1, prompt)
+            n_blocks = 3
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n_blocks):
+                blk.fill_(s.mask_id)
+                for st in range(S):
+                    if taur is None:
+                        model.diffuse_step([1], blk, B, 0.9, st == S - 1, nm)
+                    else:
+                        model.diffuse_step_revise([1], blk, B, 0.9, taur, st == S - 1, nm)
+                model.verify_block([1], blk, B, ar, acc1)
+                model.commit_kv(1, B)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            key = f"S{S}" + ("_revise" if taur is not None else "")
+            diff[key] = {"steps": S, "tau": 0.9, "tau_revise": taur, "ms_per_block": round(dt / n_blocks * 1e3, 3),
+                         "tok_per_s": round(n_blocks * B / dt, 1), "tpf": round(B / (S + 1), 3)}
+            log(f"diffusion S={S}{' revise' if taur is not None else ''}: {diff[key]['ms_per_block']} ms per block, "
+                f"{diff[key]['tok_per_s']} tok/s")
+        out["diffusion_step_budget"] = diff
         out["modes"] = {"selfspec_natural": {"cycles": 16, "tokens": int(sum(Ln)), "tok_per_s": round(sum(Ln) / t_nat, 1),
                                              "mean_accept": round(float(np.mean(Ln)), 3)},
                         "ar": {"tokens": 64, "tok_per_s": round(64 / t_ar, 1), "ms_per_token": round(t_ar / 64 * 1e3, 3)},

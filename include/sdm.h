@@ -169,6 +169,20 @@ sdm_status sdm_prefill(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32
 sdm_status sdm_diffuse_step(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, int32_t* d_block, int32_t B,
                             float tau, int32_t force_all, int32_t* d_n_masked, float* d_conf, float* d_logits);
 
+/* A denoising step that may also rewrite positions already written (the
+ * pages: in diffusion mode the model can go back and modify content it has
+ * generated -- fintech-frontier-insights "three generation modes", diffusion
+ * bullet, and the aimodeling text; the rule is this library's reading).  As
+ * sdm_diffuse_step, and from the same forward every position i of a block
+ * that does not hold MASK, whose argmax tok_i differs from its token and whose
+ * conf_i > tau_revise, takes tok_i.  Every decision is made on the block as it
+ * was before the step.  d_n_revised (nullable) [n_seq] receives the number of
+ * rewritten positions.  conf <= 1, so tau_revise >= 1 gives exactly
+ * sdm_diffuse_step.  NaN tau or tau_revise: SDM_ERR_ARG. */
+sdm_status sdm_diffuse_step_revise(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, int32_t* d_block,
+                                   int32_t B, float tau, float tau_revise, int32_t force_all, int32_t* d_n_masked,
+                                   int32_t* d_n_revised, float* d_conf, float* d_logits);
+
 /* Self-spec draft: a bidirectional forward over [anchor, MASK x (B-1)] at
  * positions n..n+B-1.  d_block_out[B] = anchor then the argmax of rows 1..B-1. */
 sdm_status sdm_draft_block(sdm_model* m, int32_t seq, const int32_t* d_anchor, int32_t B, int32_t* d_block_out,

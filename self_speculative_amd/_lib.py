@@ -57,6 +57,8 @@ SIGNATURES = {
     "sdm_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
     "sdm_diffuse_step": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_int32, c_float, c_int32,
                                    c_void_p, c_void_p, c_void_p]),
+    "sdm_diffuse_step_revise": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_int32, c_float, c_float,
+                                          c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "sdm_draft_block": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
     "sdm_verify_block": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_int32, c_void_p, c_void_p,
                                    c_void_p]),

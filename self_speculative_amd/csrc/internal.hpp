@@ -231,6 +231,8 @@ struct FinishArgs {
   int* n_masked;         // DIFFUSE: [slots]
   float* conf_out;       // DIFFUSE: optional [slots][T]
   float tau; int force_all;
+  float tau_revise;      // DIFFUSE: written positions whose argmax differs with conf > tau_revise take it
+  int* n_revised;        // DIFFUSE: optional [slots]
   int* next;             // NEXT: device token (last row of slot 0)
 };
 

@@ -1299,7 +1299,10 @@ __global__ void k_finish_mode(FinishArgs f) {
     for (int j = 0; j < T; ++j) f.ar_out[r0 + j] = f.tok[r0 + j];
     f.accept[slot] = k + 1;
   } else {  // FIN_DIFFUSE
-    int best = -1, n_m = 0, n_u = 0;
+    // masked positions: the unmask rule; written positions: the revise rule
+    // (tau_revise >= 1 never fires, conf <= 1).  Each decision reads only its
+    // own position's token before the step, and `best` is fixed first.
+    int best = -1, n_m = 0, n_u = 0, n_r = 0;
     for (int i = 0; i < T; ++i)
       if (f.block[r0 + i] == f.mask_id) {
         ++n_m;
@@ -1307,13 +1310,19 @@ __global__ void k_finish_mode(FinishArgs f) {
       }
     for (int i = 0; i < T; ++i) {
       if (f.conf_out) f.conf_out[r0 + i] = f.conf[r0 + i];
-      if (f.block[r0 + i] != f.mask_id) continue;
-      if (f.force_all || i == best || f.conf[r0 + i] > f.tau) {
-        f.block[r0 + i] = f.tok[r0 + i];
+      const int cur = f.block[r0 + i], t = f.tok[r0 + i];
+      if (cur != f.mask_id) {
+        if (t != cur && f.conf[r0 + i] > f.tau_revise) {
+          f.block[r0 + i] = t;
+          ++n_r;
+        }
+      } else if (f.force_all || i == best || f.conf[r0 + i] > f.tau) {
+        f.block[r0 + i] = t;
         ++n_u;
       }
     }
     f.n_masked[slot] = n_m - n_u;
+    if (f.n_revised) f.n_revised[slot] = n_r;
   }
 }
 

@@ -771,10 +771,17 @@ sdm_status sdm_commit_kv(sdm_model* m, int32_t seq, int32_t n_accept) {
 
 sdm_status sdm_diffuse_step(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, int32_t* d_block, int32_t B,
                             float tau, int32_t force_all, int32_t* d_n_masked, float* d_conf, float* d_logits) {
+  return sdm_diffuse_step_revise(m, n_seq, h_seq_ids, d_block, B, tau, 2.f, force_all, d_n_masked, nullptr, d_conf,
+                                 d_logits);
+}
+
+sdm_status sdm_diffuse_step_revise(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, int32_t* d_block,
+                                   int32_t B, float tau, float tau_revise, int32_t force_all, int32_t* d_n_masked,
+                                   int32_t* d_n_revised, float* d_conf, float* d_logits) {
   sdm_status s = check_model(m);
   if (s != SDM_OK) return s;
   if (!d_block || !d_n_masked) return fail(SDM_ERR_ARG, "null pointer");
-  if (!(tau == tau)) return fail(SDM_ERR_ARG, "tau is NaN");
+  if (!(tau == tau) || !(tau_revise == tau_revise)) return fail(SDM_ERR_ARG, "tau or tau_revise is NaN");
   Slots sl;
   std::vector<int32_t> ids, ends;
   if ((s = check_block_call(m, n_seq, h_seq_ids, B, &sl, &ids, &ends)) != SDM_OK) return s;
@@ -788,6 +795,8 @@ sdm_status sdm_diffuse_step(sdm_model* m, int32_t n_seq, const int32_t* h_seq_id
   fin.conf_out = d_conf;
   fin.tau = tau;
   fin.force_all = force_all ? 1 : 0;
+  fin.tau_revise = tau_revise;
+  fin.n_revised = d_n_revised;
   TokenInput ti;
   ti.tokens = d_block;
   if ((s = forward(m, sl, BIDIR, ti, false, d_logits, fin)) != SDM_OK) return s;

@@ -108,7 +108,11 @@ def generate_selfspec(model: Model, prompt, n_tokens: int, B: int, forced: Optio
 
 
 def generate_diffusion_batch(model: Model, prompts: Sequence, n_tokens: int, B: int, tau: float,
-                             max_steps: Optional[int] = None, seqs: Optional[Sequence[int]] = None) -> List[GpuGen]:
+                             max_steps: Optional[int] = None, seqs: Optional[Sequence[int]] = None,
+                             tau_revise: Optional[float] = None) -> List[GpuGen]:
+    """Block diffusion for several sequences in lockstep per block; with
+    ``tau_revise`` each step also rewrites written positions
+    (``sdm_diffuse_step_revise``)."""
     dev = model.device
     seqs = list(seqs) if seqs is not None else list(range(len(prompts)))
     for s, p in zip(seqs, prompts):
@@ -131,7 +135,10 @@ def generate_diffusion_batch(model: Model, prompts: Sequence, n_tokens: int, B: 
             idx = torch.as_tensor(active, device=dev)
             sub = blk[idx].contiguous()
             subn = nm[: len(active)]
-            model.diffuse_step([seqs[i] for i in active], sub, B, tau, force, subn)
+            if tau_revise is None:
+                model.diffuse_step([seqs[i] for i in active], sub, B, tau, force, subn)
+            else:
+                model.diffuse_step_revise([seqs[i] for i in active], sub, B, tau, tau_revise, force, subn)
             blk[idx] = sub
             nm_host[: len(active)].copy_(subn, non_blocking=True)
             model.stream.synchronize()
@@ -155,5 +162,5 @@ def generate_diffusion_batch(model: Model, prompts: Sequence, n_tokens: int, B: 
 
 
 def generate_diffusion(model: Model, prompt, n_tokens: int, B: int, tau: float, max_steps: Optional[int] = None,
-                       seq: int = 0) -> GpuGen:
-    return generate_diffusion_batch(model, [prompt], n_tokens, B, tau, max_steps, [seq])[0]
+                       seq: int = 0, tau_revise: Optional[float] = None) -> GpuGen:
+    return generate_diffusion_batch(model, [prompt], n_tokens, B, tau, max_steps, [seq], tau_revise)[0]

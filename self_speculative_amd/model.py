@@ -151,6 +151,14 @@ class Model:
         L.check(self.lib.sdm_diffuse_step(self.handle, len(seq_ids), ids, L.ptr(block), B, float(tau),
                                           int(bool(force_all)), L.ptr(n_masked), L.ptr(conf), L.ptr(logits)))
 
+    def diffuse_step_revise(self, seq_ids: Sequence[int], block: torch.Tensor, B: int, tau: float, tau_revise: float,
+                            force_all: bool, n_masked: torch.Tensor, n_revised: torch.Tensor = None,
+                            conf: torch.Tensor = None, logits: torch.Tensor = None):
+        ids = (c_int32 * len(seq_ids))(*seq_ids)
+        L.check(self.lib.sdm_diffuse_step_revise(self.handle, len(seq_ids), ids, L.ptr(block), B, float(tau),
+                                                 float(tau_revise), int(bool(force_all)), L.ptr(n_masked),
+                                                 L.ptr(n_revised), L.ptr(conf), L.ptr(logits)))
+
     def draft_block(self, seq: int, anchor: int | torch.Tensor, B: int, block_out: torch.Tensor,
                     logits: torch.Tensor = None):
         L.check(self.lib.sdm_draft_block(self.handle, seq, self._addr(anchor), B, L.ptr(block_out), L.ptr(logits)))

@@ -82,3 +82,18 @@ def unmask_exempt(block_before, sel: O.RowSel, tau: float, mask_id: int, eps=Non
         if lc[i1] - lc[i0] < max(MARGIN_EXEMPT, 2 * (e[masked][i1] + e[masked][i0])):
             return True
     return bool(np.any(sel.margin[masked] < np.maximum(MARGIN_EXEMPT, 2 * e[masked])))
+
+
+def revise_exempt(block_before, sel: O.RowSel, tau_revise: float, mask_id: int, eps, positions) -> bool:
+    """Whether differing revise decisions at ``positions`` (written, not MASK)
+    sit on a near-tie: the token decision (top-2 margin within 2 eps) or the
+    confidence within 2 eps of ln tau_revise (log scale, as for unmasking)."""
+    e = np.asarray(eps, dtype=np.float64)
+    for i in positions:
+        bar = max(MARGIN_EXEMPT, 2 * float(e[i]))
+        if sel.margin[i] < bar:
+            continue
+        if tau_revise > 0 and abs(math.log(sel.conf[i]) - math.log(tau_revise)) < bar:
+            continue
+        return False
+    return True

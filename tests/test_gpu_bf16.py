@@ -137,6 +137,72 @@ def test_bf16_lockstep_diffusion(gm, om):
     assert rep.max_logit_err <= 2e-2
 
 
+def test_bf16_lockstep_diffusion_with_revision(gm, om):
+    """Revision variant in lockstep: masked positions by the unmask rule,
+    written ones rewritten to a differing argmax whose conf clears tau_revise."""
+    seq = 1
+    gm.seq_reset(seq)
+    rep = Report()
+    p = W.prompt_ids(SHAPE, 70, seed=28)
+    sess = O.OracleSession(om)
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    gm.prefill(seq, _i32(p), nxt)
+    sess.prefill(0, p)
+    lg = torch.empty((B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+    nm = torch.empty(1, dtype=torch.int32, device=DEV)
+    nr = torch.empty(1, dtype=torch.int32, device=DEV)
+    blk = np.full(B, SHAPE.mask_id, dtype=np.int32)
+    blk[:6] = W.prompt_ids(SHAPE, 6, seed=29)
+    revised = 0
+    for s, (tau, taur) in enumerate([(0.9, 0.0), (0.0012, 0.0), (0.9, 0.0011), (0.9, 0.0)]):
+        force = s == 3
+        print(f"bf16 revise step {s} tau={tau} tau_revise={taur} force={force}", flush=True)
+        gblk = _i32(blk)
+        gm.diffuse_step_revise([seq], gblk, B, tau, taur, force, nm, nr, None, lg)
+        new, U, R, left, sel = sess.diffuse_step_revise(0, blk, tau, taur, force)
+        torch.cuda.synchronize()
+        eps = rep.logits(lg, sel.logits)
+        got = gblk.cpu().numpy()
+        if not np.array_equal(got, new):
+            from lockstep import revise_exempt, unmask_exempt
+            diff = np.nonzero(got != new)[0]
+            masked = blk == SHAPE.mask_id
+            assert (not masked[diff].all() or unmask_exempt(blk, sel, tau, SHAPE.mask_id, eps)), (got, new)
+            assert revise_exempt(blk, sel, taur, SHAPE.mask_id, eps, diff[~masked[diff]]), (got, new)
+            rep.resyncs += 1
+        else:
+            assert int(nm.item()) == left and int(nr.item()) == len(R)
+        revised += len(R)
+        blk = new
+    assert (blk != SHAPE.mask_id).all() and revised > 0
+    print(f"bf16 revision lockstep: max|dlogit| {rep.max_logit_err:.3e}, revised {revised}, resyncs {rep.resyncs}",
+          flush=True)
+    assert rep.max_logit_err <= 2e-2
+
+
+def test_bf16_revise_disabled_equals_plain_step(gm):
+    p = W.prompt_ids(SHAPE, 40, seed=30)
+    outs = []
+    for variant in ("plain", "revise_off"):
+        gm.seq_reset(2)
+        nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+        gm.prefill(2, _i32(p), nxt)
+        blk = torch.full((1, B), SHAPE.mask_id, dtype=torch.int32, device=DEV)
+        blk[0, :4] = 5
+        nm = torch.empty(1, dtype=torch.int32, device=DEV)
+        conf = torch.empty(B, dtype=torch.float32, device=DEV)
+        lg = torch.empty((B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+        print(f"bf16 diffuse step {variant}", flush=True)
+        if variant == "plain":
+            gm.diffuse_step([2], blk, B, 0.0012, False, nm, conf, lg)
+        else:
+            gm.diffuse_step_revise([2], blk, B, 0.0012, 1.0, False, nm, None, conf, lg)
+        torch.cuda.synchronize()
+        outs.append((blk.cpu().numpy(), nm.cpu().numpy(), conf.cpu().numpy(), lg.cpu().numpy()))
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_bf16_selfspec_equals_ar_on_gpu(gm):
     """The GPU path is row-independent: a causal block forward reproduces the
     one-row AR forward bit for bit, so self-spec emits exactly the AR stream."""

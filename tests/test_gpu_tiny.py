@@ -49,6 +49,44 @@ def test_tiny_streams_equal_golden(gm):
     assert df.tokens == GOLD["diffusion"] and df.steps_per_block == GOLD["diffusion_steps"]
 
 
+@pytest.mark.parametrize("tau,S", [(1.01, None), (0.0045, 3)])
+def test_tiny_diffusion_with_revision(gm, om, tau, S):
+    """The revision variant: every written position whose argmax differs is
+    rewritten (tau_revise 0), so only argmax decisions are involved."""
+    from self_speculative_amd import decode as D
+    p = W.prompt_ids(TINY, 13, seed=6)
+    print(f"tiny diffusion with revision tau={tau} S={S}", flush=True)
+    g = D.generate_diffusion(gm, p, 32, 8, tau, S, seq=_fresh(gm, 5), tau_revise=0.0)
+    o = O.generate_diffusion(om, p, 32, 8, tau, S, tau_revise=0.0)
+    assert g.tokens == o.tokens and g.steps_per_block == o.steps_per_block
+    if tau > 1:
+        assert sum(o.revisions) > 0
+
+
+def test_tiny_revise_step_counts(gm, om):
+    """Step by step: blocks and the per-sequence revise counts equal the oracle's."""
+    seq = _fresh(gm, 6)
+    p = W.prompt_ids(TINY, 9, seed=7)
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    gm.prefill(seq, torch.as_tensor(p, device="cuda"), nxt)
+    sess = O.OracleSession(om)
+    sess.prefill(0, p)
+    blk = np.full(8, TINY.mask_id, dtype=np.int32)
+    blk[[2, 5]] = [11, 40]                               # written positions the step may revise
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    nr = torch.empty(1, dtype=torch.int32, device="cuda")
+    # tau_revise far from the tiny model's confidences (about 1/256): this test has no exemptions
+    for step, (tau, taur) in enumerate([(1.01, 0.0), (0.0045, 0.5), (1.01, 2.0), (0.9, 0.0)]):
+        print(f"tiny revise step {step}", flush=True)
+        g = torch.as_tensor(blk, device="cuda")
+        gm.diffuse_step_revise([seq], g, 8, tau, taur, False, nm, nr)
+        new, U, R, left, sel = sess.diffuse_step_revise(0, blk, tau, taur, False)
+        torch.cuda.synchronize()
+        assert g.cpu().tolist() == new.tolist()
+        assert int(nm.item()) == left and int(nr.item()) == len(R)
+        blk = new
+
+
 @pytest.mark.parametrize("tau,S", [(1.01, None), (0.0, None), (0.0045, 3), (0.9, 4)])
 def test_tiny_diffusion_thresholds(gm, om, tau, S):
     from self_speculative_amd import decode as D
