@@ -15,5 +15,7 @@ worked example); the per-step rule itself is pinned.
 from .model import (BIDIR, CAUSAL, INT4_GROUP, KVCache, OracleModel, apply_rope, attention, bf16_pair_round,
                     bf16_round, decode_bf16_bits, dequant_int4, int4_codes, rms_normalize, rope_tables, select_rows,
                     silu, visible)
-from .modes import (GenResult, OracleSession, RowSel, accept_length, generate_ar, generate_diffusion,
-                    generate_diffusion_batch, generate_selfspec, revise_rule, unmask_rule)
+from .modes import (GenResult, OracleSession, RowSel, accept_length, generate_ar, generate_ar_sample,
+                    generate_diffusion, generate_diffusion_batch, generate_selfspec, generate_selfspec_sample,
+                    revise_rule, unmask_rule)
+from . import sampling

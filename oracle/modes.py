@@ -41,6 +41,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 from .model import BIDIR, CAUSAL, KVCache, OracleModel, select_rows
+from . import sampling as SP
 
 
 @dataclass
@@ -181,6 +182,69 @@ class OracleSession:
         return new, U, R, n_left, sel
 
 
+    # -- sampling at temperature T > 0 (see oracle/sampling.py) ---------------
+    # A sampled token's position is the absolute position it will occupy:
+    # prefill of P tokens -> P; an AR step on the token at position n -> n + 1;
+    # draft row j -> n + j; verify row j -> n + j + 1.
+    def prefill_sample(self, seq: int, tokens: Sequence[int], T: float, seed: int) -> SP.Sample:
+        c = self._cache(seq)
+        assert c.n == 0
+        logits = self.model.forward(c, tokens, CAUSAL, logits_rows=[len(tokens) - 1])
+        c.n = len(tokens)
+        self.forwards += 1
+        return SP.sample_row(logits[0], T, seed, seq, len(tokens), SP.PURPOSE_SAMPLE, self.mask_id)
+
+    def decode_ar_sample(self, seq: int, token: int, T: float, seed: int):
+        c = self._cache(seq)
+        n = c.n
+        logits = self.model.forward(c, [token], CAUSAL)
+        c.n += 1
+        self.forwards += 1
+        return SP.sample_row(logits[0], T, seed, seq, n + 1, SP.PURPOSE_SAMPLE, self.mask_id), logits
+
+    def draft_block_sample(self, seq: int, anchor: int, B: int, T: float, seed: int):
+        """Bidirectional forward over [anchor, MASK x (B-1)]; row j >= 1 draws
+        d_j (purpose DRAFT, position n + j).  -> (block, logits, samples)."""
+        c = self._cache(seq)
+        n = c.n
+        blk = np.full(B, self.mask_id, dtype=np.int32)
+        blk[0] = anchor
+        logits = self.model.forward(c, blk, BIDIR)
+        self.forwards += 1
+        smp = [None] + [SP.sample_row(logits[j], T, seed, seq, n + j, SP.PURPOSE_DRAFT, self.mask_id)
+                        for j in range(1, B)]
+        for j in range(1, B):
+            blk[j] = smp[j].tok
+        return blk, logits, smp
+
+    def verify_block_sample(self, seq: int, block: Sequence[int], draft_logits: np.ndarray, T: float, seed: int):
+        """Causal forward over the drafted block; rejection-sampling verify.
+        -> (L, emitted token, verify logits, details): L - 1 drafts accepted,
+        the emitted token follows them (a residual draw at the first
+        rejection, else the bonus from the last row)."""
+        c = self._cache(seq)
+        n = c.n
+        block = np.asarray(block, dtype=np.int32)
+        B = len(block)
+        logits = self.model.forward(c, block, CAUSAL)
+        self.forwards += 1
+        k = 0
+        margins = []
+        for j in range(1, B):
+            logp = float(SP.log_softmax_T(logits[j - 1], T, self.mask_id)[block[j]])
+            logq = float(SP.log_softmax_T(draft_logits[j], T, self.mask_id)[block[j]])
+            ok, d = SP.accept_draft(logp, logq, seed, seq, n + j)
+            margins.append(d)
+            if not ok:
+                break
+            k += 1
+        if k < B - 1:
+            out = SP.residual_sample(logits[k], draft_logits[k + 1], T, seed, seq, n + k + 1, self.mask_id)
+        else:
+            out = SP.sample_row(logits[B - 1], T, seed, seq, n + B, SP.PURPOSE_SAMPLE, self.mask_id)
+        return k + 1, out.tok, logits, {"accept_margins": margins, "emitted": out}
+
+
 # -- generation loops -----------------------------------------------------------
 @dataclass
 class GenResult:
@@ -269,3 +333,31 @@ def generate_diffusion_batch(model: OracleModel, prompts: Sequence[Sequence[int]
     never interact, so this is each sequence decoded on its own."""
     return [generate_diffusion(model, p, n_tokens, B, tau, max_steps, seq=i, tau_revise=tau_revise)
             for i, p in enumerate(prompts)]
+
+
+def generate_ar_sample(model: OracleModel, prompt: Sequence[int], n_tokens: int, T: float, seed: int,
+                       seq: int = 0) -> GenResult:
+    """AR sampling at temperature T (purpose SAMPLE at every position)."""
+    sess = OracleSession(model, keep_logits=False)
+    first = sess.prefill_sample(seq, prompt, T, seed)
+    toks = [first.tok]
+    while len(toks) < n_tokens:
+        smp, _ = sess.decode_ar_sample(seq, toks[-1], T, seed)
+        toks.append(smp.tok)
+    return GenResult(toks, sess.forwards - 1)
+
+
+def generate_selfspec_sample(model: OracleModel, prompt: Sequence[int], n_tokens: int, B: int, T: float,
+                             seed: int, seq: int = 0) -> GenResult:
+    """Self-speculation at temperature T with the rejection-sampling verify."""
+    sess = OracleSession(model, keep_logits=False)
+    first = sess.prefill_sample(seq, prompt, T, seed)
+    toks = [first.tok]
+    Ls: List[int] = []
+    while len(toks) < n_tokens:
+        blk, dlog, _ = sess.draft_block_sample(seq, toks[-1], B, T, seed)
+        L, nxt, _, _ = sess.verify_block_sample(seq, blk, dlog, T, seed)
+        sess.commit_kv(seq, L)
+        toks += [int(t) for t in blk[1:L]] + [int(nxt)]
+        Ls.append(L)
+    return GenResult(toks[:n_tokens], sess.forwards - 1, accept_lengths=Ls)
