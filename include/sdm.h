@@ -200,6 +200,45 @@ sdm_status sdm_verify_block(sdm_model* m, int32_t n_seq, const int32_t* h_seq_id
  * causal block forward of seq.  Requires a preceding sdm_verify_block on seq. */
 sdm_status sdm_commit_kv(sdm_model* m, int32_t seq, int32_t n_accept);
 
+/* Sampling at temperature > 0 (one sequence per call).  The pages state the
+ * self-speculation identity only at temperature 0 and leave higher
+ * temperatures open (fintech-frontier-insights, self-speculation bullet); these
+ * calls are this library's reading: the standard lossless rejection-sampling
+ * verify, under which self-speculation emits tokens distributed as AR sampling
+ * at the same temperature.
+ *   Random numbers: Philox4x64-10 (Salmon et al., "Parallel random numbers: as
+ *   easy as 1, 2, 3") under key (seed, 0) and counter (vocab id / 4, position,
+ *   sequence id, purpose: 1 draft, 2 accept, 3 residual, 4 sample); a 64-bit
+ *   output x is the uniform u = ((x >> 40) + 1/2) * 2^-24.  A token's position
+ *   is the absolute position it will occupy.
+ *   A row is sampled from softmax(l / T) over non-MASK ids by the Gumbel-max
+ *   trick: argmax of l_v / T - ln(-ln u_v), lowest id on ties.
+ * temperature must be finite and > 0 (else SDM_ERR_ARG); the other arguments
+ * and state rules are those of the greedy calls. */
+/* As sdm_prefill; the first generated token (position n) is sampled. */
+sdm_status sdm_prefill_sample(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32_t n, float temperature,
+                              uint64_t seed, int32_t* d_next_token, float* d_logits);
+/* As sdm_decode_ar; the next token (position len + 1) is sampled. */
+sdm_status sdm_decode_ar_sample(sdm_model* m, int32_t seq, const int32_t* d_token, float temperature, uint64_t seed,
+                                int32_t* d_next_token, float* d_logits);
+/* As sdm_draft_block; rows 1..B-1 are sampled (purpose draft, positions n + j)
+ * instead of argmax.  d_draft_logits [B][vocab] fp32 receives the draft's
+ * logits and d_draft_stats [2][B] fp32 ln q(d_j) and the row's
+ * ln sum exp(l / T); both are inputs of sdm_verify_block_sample.  B >= 2. */
+sdm_status sdm_draft_block_sample(sdm_model* m, int32_t seq, const int32_t* d_anchor, int32_t B, float temperature,
+                                  uint64_t seed, int32_t* d_block_out, float* d_draft_logits, float* d_draft_stats);
+/* Causal forward over the drafted block; draft j (1..B-1) is accepted while
+ * ln u_j < ln p_j(d_j) - ln q_j(d_j) (p_j from verify row j - 1, u_j purpose
+ * accept at position n + j).  d_accept_len[0] = L = accepted + 1;
+ * d_next_token[0] = the token after the accepted drafts: at the first
+ * rejection j a Gumbel-max draw from max(0, p_j - q_j) (purpose residual,
+ * position n + j), else a draw from the last row (purpose sample, position
+ * n + B).  Commit with sdm_commit_kv(seq, L) as after sdm_verify_block.
+ * B >= 2, the same temperature and seed as the draft. */
+sdm_status sdm_verify_block_sample(sdm_model* m, int32_t seq, const int32_t* d_block, int32_t B, float temperature,
+                                   uint64_t seed, const float* d_draft_logits, const float* d_draft_stats,
+                                   int32_t* d_accept_len, int32_t* d_next_token, float* d_logits);
+
 /* AR: causal forward over d_token[0] at position n, commit it, d_next_token[0]
  * = argmax. */
 sdm_status sdm_decode_ar(sdm_model* m, int32_t seq, const int32_t* d_token, int32_t* d_next_token, float* d_logits);

@@ -340,11 +340,12 @@ def generate_ar_sample(model: OracleModel, prompt: Sequence[int], n_tokens: int,
     """AR sampling at temperature T (purpose SAMPLE at every position)."""
     sess = OracleSession(model, keep_logits=False)
     first = sess.prefill_sample(seq, prompt, T, seed)
-    toks = [first.tok]
+    toks, gaps = [first.tok], [first.gap]
     while len(toks) < n_tokens:
         smp, _ = sess.decode_ar_sample(seq, toks[-1], T, seed)
         toks.append(smp.tok)
-    return GenResult(toks, sess.forwards - 1)
+        gaps.append(smp.gap)
+    return GenResult(toks, sess.forwards - 1, margins=gaps)
 
 
 def generate_selfspec_sample(model: OracleModel, prompt: Sequence[int], n_tokens: int, B: int, T: float,
@@ -354,10 +355,12 @@ def generate_selfspec_sample(model: OracleModel, prompt: Sequence[int], n_tokens
     first = sess.prefill_sample(seq, prompt, T, seed)
     toks = [first.tok]
     Ls: List[int] = []
+    margins = [first.gap]       # every decision's distance from flipping (Gumbel gaps, |ln u - ln p/q|)
     while len(toks) < n_tokens:
-        blk, dlog, _ = sess.draft_block_sample(seq, toks[-1], B, T, seed)
-        L, nxt, _, _ = sess.verify_block_sample(seq, blk, dlog, T, seed)
+        blk, dlog, smp = sess.draft_block_sample(seq, toks[-1], B, T, seed)
+        L, nxt, _, det = sess.verify_block_sample(seq, blk, dlog, T, seed)
+        margins += [x.gap for x in smp[1:]] + [abs(d) for d in det["accept_margins"]] + [det["emitted"].gap]
         sess.commit_kv(seq, L)
         toks += [int(t) for t in blk[1:L]] + [int(nxt)]
         Ls.append(L)
-    return GenResult(toks[:n_tokens], sess.forwards - 1, accept_lengths=Ls)
+    return GenResult(toks[:n_tokens], sess.forwards - 1, accept_lengths=Ls, margins=margins)

@@ -25,7 +25,8 @@ Self-speculation at T: the draft samples d_j from its row j (q_j, purpose
 DRAFT, position n + j); the verify forward's row j - 1 gives p_j.  Draft j is
 accepted iff ln u_j < ln p_j(d_j) - ln q_j(d_j) (purpose ACCEPT); at the first
 rejection j the emitted token is a Gumbel-max draw from the weights
-max(0, p_j - q_j) (purpose RESIDUAL, position n + j), otherwise the bonus is a
+max(0, p_j - q_j) (purpose RESIDUAL, position n + j; should rounding leave no
+id with p > q, the p row's own draw, purpose SAMPLE), otherwise the bonus is a
 draw from the verify's last row (purpose SAMPLE, position n + B).  AR sampling
 draws each token from its row with purpose SAMPLE.
 """
@@ -142,6 +143,8 @@ def residual_sample(p_logits: np.ndarray, q_logits: np.ndarray, T: float, seed: 
     p = np.exp(log_softmax_T(p_logits, T, mask_id))
     q = np.exp(log_softmax_T(q_logits, T, mask_id))
     w = p - q
+    if not (w > 0).any():   # p == q to rounding: the p row's own sample at this position
+        return sample_row(p_logits, T, seed, seq, position, PURPOSE_SAMPLE, mask_id)
     with np.errstate(divide="ignore"):
         lw = np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf)
     s = gumbel_argmax(lw, gumbel_noise(len(lw), position, seq, PURPOSE_RESIDUAL, seed))

@@ -59,6 +59,12 @@ SIGNATURES = {
                                    c_void_p, c_void_p, c_void_p]),
     "sdm_diffuse_step_revise": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_int32, c_float, c_float,
                                           c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "sdm_prefill_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_float, c_uint64, c_void_p, c_void_p]),
+    "sdm_decode_ar_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_float, c_uint64, c_void_p, c_void_p]),
+    "sdm_draft_block_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_float, c_uint64, c_void_p,
+                                         c_void_p, c_void_p]),
+    "sdm_verify_block_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_float, c_uint64, c_void_p,
+                                          c_void_p, c_void_p, c_void_p, c_void_p]),
     "sdm_draft_block": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
     "sdm_verify_block": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_int32, c_void_p, c_void_p,
                                    c_void_p]),

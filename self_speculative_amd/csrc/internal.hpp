@@ -16,7 +16,18 @@ constexpr int kAttnStagedPairs = 256;  // (split, KV head) pairs from which atte
 
 enum Mode { CAUSAL = 0, BIDIR = 1 };
 enum Epi { EPI_QKV = 0, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
-enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3 };
+enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3,
+              FIN_SAMPLE_NEXT = 4, FIN_SAMPLE_DRAFT = 5, FIN_SAMPLE_VERIFY = 6 };
+// Random-number purposes of the sampling modes (counter word 3).
+enum Purpose { PURPOSE_DRAFT = 1, PURPOSE_ACCEPT = 2, PURPOSE_RESIDUAL = 3, PURPOSE_SAMPLE = 4 };
+constexpr int kSampleParts = 64;  // workgroups sharing one row's vocabulary when sampling
+
+// One workgroup's share of a sampled row: the two best perturbed scores (the
+// best's id, lowest on ties) and the row's max and sum of exp(z - max).
+struct SamplePart {
+  float best, second, m, s;
+  int idx, pad0, pad1, pad2;
+};
 enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1 };
 
 // Activations of the bf16 path travel between kernels as two bf16 planes, hi
@@ -233,6 +244,16 @@ struct FinishArgs {
   float tau; int force_all;
   float tau_revise;      // DIFFUSE: written positions whose argmax differs with conf > tau_revise take it
   int* n_revised;        // DIFFUSE: optional [slots]
+  // sampling modes (one sequence): rows' logits [M][V] at temperature 1 / inv_t
+  const float* logits; int V; float inv_t; uint64_t seed; int seq_id;
+  int target_pos;        // SAMPLE_NEXT: position of the token the last row predicts
+  SamplePart* parts;     // [M][kSampleParts]
+  float* lse;            // [M] ln sum_v exp(l_v / T) over non-MASK ids
+  float* gap;            // [M] best minus second perturbed score
+  float* logp;           // [M] ln p(sampled token)
+  float* logp_probe;     // VERIFY: [M] ln p(block[t + 1]) of row t
+  float* draft_stats;    // DRAFT out / VERIFY in: [2][T] ln q(d_t), lse of draft row t
+  const float* draft_logits;  // VERIFY: the draft forward's logits [T][V]
   int* next;             // NEXT: device token (last row of slot 0)
 };
 

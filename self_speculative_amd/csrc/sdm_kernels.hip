@@ -1326,7 +1326,232 @@ __global__ void k_finish_mode(FinishArgs f) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sampling at temperature T > 0 (one sequence).  Random numbers are
+// Philox4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2,
+// 3") under key (seed, 0) and counter (vocab id / 4, position, sequence,
+// purpose); a 64-bit word x gives u = ((x >> 40) + 1/2) * 2^-24.  A row is
+// sampled by the Gumbel-max trick: tok = argmax over non-MASK v of
+// l_v / T - ln(-ln u_v), lowest id on ties.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+__device__ __forceinline__ float uniform24(uint64_t x) {
+  return ((float)(uint32_t)(x >> 40) + 0.5f) * 5.9604644775390625e-8f;  // 2^-24, exact
+}
+
+__device__ __forceinline__ void part_push(SamplePart& a, float score, int v) {
+  if (score > a.best) {  // ids arrive in increasing order: strict > keeps the lowest on ties
+    a.second = a.best;
+    a.best = score;
+    a.idx = v;
+  } else if (score > a.second) {
+    a.second = score;
+  }
+}
+__device__ __forceinline__ void part_merge(SamplePart& a, const SamplePart& b) {
+  // b covers higher ids than a, so a wins ties
+  if (b.best > a.best) {
+    a.second = fmaxf(a.best, b.second);
+    a.best = b.best;
+    a.idx = b.idx;
+  } else {
+    a.second = fmaxf(a.second, b.best);
+  }
+  if (b.s > 0.f) {
+    if (a.s == 0.f) {
+      a.m = b.m;
+      a.s = b.s;
+    } else {
+      const float mm = fmaxf(a.m, b.m);
+      a.s = a.s * __expf(a.m - mm) + b.s * __expf(b.m - mm);
+      a.m = mm;
+    }
+  }
+}
+__device__ __forceinline__ SamplePart part_empty() {
+  SamplePart p;
+  p.best = p.second = -INFINITY;
+  p.m = -INFINITY;
+  p.s = 0.f;
+  p.idx = 0x7fffffff;
+  p.pad0 = p.pad1 = p.pad2 = 0;
+  return p;
+}
+
+// The workgroup's partial merged by thread 0 in thread order (deterministic).
+__device__ void part_reduce_store(SamplePart mine, SamplePart* out) {
+  __shared__ SamplePart sp[256];
+  sp[threadIdx.x] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    SamplePart a = sp[0];
+    for (int t = 1; t < 256; ++t) part_merge(a, sp[t]);
+    *out = a;
+  }
+}
+
+// Row scan for sampling.  Grid (kSampleParts, rows); row r of the launch is
+// logits row r0 + r with target position pos0 + r.  Thread t of part q takes
+// the 4-id chunks q * cpp + t, q * cpp + t + 256, ... (cpp chunks per part);
+// ids inside a thread's chunks arrive in increasing order.
+__global__ __launch_bounds__(256) void k_sample_partial(FinishArgs f, int r0, int pos0, int purpose) {
+  const int r = r0 + blockIdx.y;
+  const float* row = f.logits + (int64_t)r * f.V;
+  const int nch = (f.V + 3) / 4, cpp = (nch + kSampleParts - 1) / kSampleParts;
+  const int c_end = min(nch, (blockIdx.x + 1) * cpp);
+  SamplePart a = part_empty();
+  float m = -INFINITY, sum = 0.f;
+  for (int c = blockIdx.x * cpp + threadIdx.x; c < c_end; c += 256) {
+    uint64_t w[4] = {(uint64_t)c, (uint64_t)(pos0 + blockIdx.y), (uint64_t)f.seq_id, (uint64_t)purpose};
+    philox4x64_10(w, f.seed, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * c + e;
+      if (v >= f.V || v == f.mask_id) continue;
+      const float z = row[v] * f.inv_t;
+      part_push(a, z - logf(-logf(uniform24(w[e]))), v);
+      if (z > m) {
+        sum = sum * __expf(m - z) + 1.f;
+        m = z;
+      } else {
+        sum += __expf(z - m);
+      }
+    }
+  }
+  a.m = m;
+  a.s = sum;
+  part_reduce_store(a, f.parts + (int64_t)r * kSampleParts + blockIdx.x);
+}
+
+// Merge a row's parts (part order): tok, gap, lse, ln p(tok) and, with a
+// probe, ln p(probe).  One thread per row of the launch.
+__global__ void k_sample_merge(FinishArgs f, int r0, int nrows, const int* probe) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nrows) return;
+  const int r = r0 + i;
+  const SamplePart* pp = f.parts + (int64_t)r * kSampleParts;
+  SamplePart a = pp[0];
+  for (int q = 1; q < kSampleParts; ++q) part_merge(a, pp[q]);
+  const float lse = a.m + logf(a.s);
+  const float* row = f.logits + (int64_t)r * f.V;
+  f.tok[r] = a.idx;
+  f.lse[r] = lse;
+  f.gap[r] = a.best - a.second;
+  f.logp[r] = row[a.idx] * f.inv_t - lse;
+  if (probe) f.logp_probe[r] = row[probe[i]] * f.inv_t - lse;
+}
+
+// Acceptance loop of the sampled verify (one thread): draft j is accepted iff
+// ln u_j < ln p_j(d_j) - ln q_j(d_j); accept = k + 1 for k accepted drafts.
+// With every draft accepted the emitted token is the last row's sample.
+__global__ void k_finish_sample_verify(FinishArgs f) {
+  if (threadIdx.x != 0) return;
+  const int T = f.T, n = f.slots.len[0];
+  int k = 0;
+  for (int j = 1; j < T; ++j) {
+    uint64_t w[4] = {0, (uint64_t)(n + j), (uint64_t)f.seq_id, (uint64_t)PURPOSE_ACCEPT};
+    philox4x64_10(w, f.seed, 0);
+    if (!(logf(uniform24(w[0])) < f.logp_probe[j - 1] - f.draft_stats[j])) break;
+    ++k;
+  }
+  f.accept[0] = k + 1;
+  if (k == T - 1) f.next[0] = f.tok[T - 1];
+}
+
+// Residual draw at the first rejection k + 1 (skipped when every draft was
+// accepted): Gumbel-max over ln(p_v - q_v) where p_v > q_v, p from verify row
+// k, q from draft row k + 1.  Grid kSampleParts.
+__global__ __launch_bounds__(256) void k_residual_partial(FinishArgs f) {
+  const int k = f.accept[0] - 1;
+  if (k >= f.T - 1) return;
+  const int n = f.slots.len[0];
+  const float* prow = f.logits + (int64_t)k * f.V;
+  const float* qrow = f.draft_logits + (int64_t)(k + 1) * f.V;
+  const float lp = f.lse[k], lq = f.draft_stats[f.T + k + 1];
+  const int nch = (f.V + 3) / 4, cpp = (nch + kSampleParts - 1) / kSampleParts;
+  const int c_end = min(nch, (blockIdx.x + 1) * cpp);
+  SamplePart a = part_empty();
+  for (int c = blockIdx.x * cpp + threadIdx.x; c < c_end; c += 256) {
+    uint64_t w[4] = {(uint64_t)c, (uint64_t)(n + k + 1), (uint64_t)f.seq_id, (uint64_t)PURPOSE_RESIDUAL};
+    philox4x64_10(w, f.seed, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * c + e;
+      if (v >= f.V || v == f.mask_id) continue;
+      const float d = __expf(prow[v] * f.inv_t - lp) - __expf(qrow[v] * f.inv_t - lq);
+      if (d > 0.f) part_push(a, logf(d) - logf(-logf(uniform24(w[e]))), v);
+    }
+  }
+  part_reduce_store(a, f.parts + blockIdx.x);
+}
+
+__global__ void k_residual_merge(FinishArgs f) {
+  const int k = f.accept[0] - 1;
+  if (threadIdx.x != 0 || k >= f.T - 1) return;
+  SamplePart a = f.parts[0];
+  for (int q = 1; q < kSampleParts; ++q) part_merge(a, f.parts[q]);
+  // no id with p > q left after rounding: the verify row's own sample at that position
+  f.next[0] = a.idx == 0x7fffffff ? f.tok[k] : a.idx;
+}
+
+__global__ void k_finish_sample_draft(FinishArgs f) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= f.T) return;
+  if (j == 0) {
+    f.block[0] = f.anchor[0];
+    return;
+  }
+  f.block[j] = f.tok[j];
+  f.draft_stats[j] = f.logp[j];
+  f.draft_stats[f.T + j] = f.lse[j];
+}
+
+__global__ void k_finish_sample_next(FinishArgs f) {
+  if (threadIdx.x == 0) f.next[0] = f.tok[f.M - 1];
+}
+
+static hipError_t launch_finish_sample(const FinishArgs& f, hipStream_t st) {
+  const int n = f.slots.len[0];
+  if (f.mode == FIN_SAMPLE_NEXT) {
+    // the last row's logits predict target_pos
+    SDM_LAUNCH(k_sample_partial, dim3(kSampleParts, 1), dim3(256), 0, st, f, f.M - 1, f.target_pos,
+               (int)PURPOSE_SAMPLE);
+    SDM_LAUNCH(k_sample_merge, dim3(1), dim3(64), 0, st, f, f.M - 1, 1, (const int*)nullptr);
+    SDM_LAUNCH(k_finish_sample_next, dim3(1), dim3(64), 0, st, f);
+  } else if (f.mode == FIN_SAMPLE_DRAFT) {
+    // bidirectional rows 1..T-1 predict their own positions n + t
+    SDM_LAUNCH(k_sample_partial, dim3(kSampleParts, f.T - 1), dim3(256), 0, st, f, 1, n + 1, (int)PURPOSE_DRAFT);
+    SDM_LAUNCH(k_sample_merge, dim3((f.T + 62) / 64), dim3(64), 0, st, f, 1, f.T - 1, (const int*)nullptr);
+    SDM_LAUNCH(k_finish_sample_draft, dim3((f.T + 63) / 64), dim3(64), 0, st, f);
+  } else {
+    // causal rows 0..T-1 predict n + t + 1; row t probes draft token block[t + 1]
+    SDM_LAUNCH(k_sample_partial, dim3(kSampleParts, f.T), dim3(256), 0, st, f, 0, n + 1, (int)PURPOSE_SAMPLE);
+    SDM_LAUNCH(k_sample_merge, dim3((f.T + 62) / 64), dim3(64), 0, st, f, 0, f.T - 1, (const int*)(f.block + 1));
+    SDM_LAUNCH(k_sample_merge, dim3(1), dim3(64), 0, st, f, f.T - 1, 1, (const int*)nullptr);
+    SDM_LAUNCH(k_finish_sample_verify, dim3(1), dim3(64), 0, st, f);
+    SDM_LAUNCH(k_residual_partial, dim3(kSampleParts), dim3(256), 0, st, f);
+    SDM_LAUNCH(k_residual_merge, dim3(1), dim3(64), 0, st, f);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_finish(const FinishArgs& f, hipStream_t st) {
+  if (f.mode >= FIN_SAMPLE_NEXT) return launch_finish_sample(f, st);
   SDM_LAUNCH(k_select_rows, dim3(f.M), dim3(256), 0, st, f.records, f.n_vtiles, f.tok, f.conf, f.margin);
   SDM_LAUNCH(k_finish_mode, dim3(f.slots.n_seq), dim3(64), 0, st, f);
   return hipGetLastError();

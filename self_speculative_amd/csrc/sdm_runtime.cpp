@@ -102,7 +102,7 @@ Dims dims_of(const sdm_config* c) {
 
 struct Layout {
   int64_t x, xn, q, attn, hbuf, ybuf, part, opart, mlpart, records, tok, conf, margin, rope_cos, rope_sin,
-      page_table, total;
+      page_table, slog, sparts, slse, sgap, slogp, sprobe, total;
 };
 
 Layout layout_of(const sdm_config* c) {
@@ -140,6 +140,13 @@ Layout layout_of(const sdm_config* c) {
   Lo.rope_cos = take((int64_t)c->max_context * (D.hd / 2) * 4);
   Lo.rope_sin = take((int64_t)c->max_context * (D.hd / 2) * 4);
   Lo.page_table = take((int64_t)c->max_seqs * D.max_pages * 4);
+  // sampling at temperature > 0: the rows' logits (bf16 models; f32 ones keep them in ybuf), per-row parts
+  Lo.slog = take(D.bf16 ? (int64_t)D.R * D.V * 4 : 0);
+  Lo.sparts = take((int64_t)D.R * kSampleParts * (int64_t)sizeof(SamplePart));
+  Lo.slse = take((int64_t)D.R * 4);
+  Lo.sgap = take((int64_t)D.R * 4);
+  Lo.slogp = take((int64_t)D.R * 4);
+  Lo.sprobe = take((int64_t)D.R * 4);
   Lo.total = off;
   return Lo;
 }
@@ -401,6 +408,8 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
           "final rmsnorm");
   ea.M = ML;
   ea.logits = d_logits;
+  const bool sampling = fin.mode >= FIN_SAMPLE_NEXT;
+  if (sampling && D.bf16 && !d_logits) ea.logits = m->at<float>(m->lo.slog);
   if (D.bf16) {
     TimedScope ts(m, SDM_K_LM_HEAD);
     HIP_TRY(launch_gemm_bf16(EPI_LOGITS, (const uint16_t*)m->lm_head, (const uint16_t*)xn, D.xn_plane,
@@ -419,6 +428,15 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
   fin.margin = m->at<float>(m->lo.margin);
   fin.mask_id = m->cfg.mask_id;
   fin.M = ML;
+  if (sampling) {
+    fin.logits = D.bf16 ? ea.logits : m->at<float>(m->lo.ybuf);
+    fin.V = D.V;
+    fin.parts = m->at<SamplePart>(m->lo.sparts);
+    fin.lse = m->at<float>(m->lo.slse);
+    fin.gap = m->at<float>(m->lo.sgap);
+    fin.logp = m->at<float>(m->lo.slogp);
+    fin.logp_probe = m->at<float>(m->lo.sprobe);
+  }
   { TimedScope ts(m, SDM_K_FINISH);
     HIP_TRY(launch_finish(fin, st), "finish"); }
   m->last_rows = ML;
@@ -658,8 +676,47 @@ sdm_status sdm_timing_stop(sdm_model* m, int64_t* launches, double* total_ms, do
   return SDM_OK;
 }
 
+namespace {
+struct Sampling {
+  bool on = false;
+  float inv_t = 1.f;
+  uint64_t seed = 0;
+};
+
+sdm_status check_sampling(float temperature, uint64_t seed, Sampling* smp) {
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return fail(SDM_ERR_ARG, "temperature must be finite and > 0");
+  smp->on = true;
+  smp->inv_t = 1.f / temperature;
+  smp->seed = seed;
+  return SDM_OK;
+}
+
+void set_sampling(FinishArgs& fin, const Sampling& smp, int seq) {
+  fin.inv_t = smp.inv_t;
+  fin.seed = smp.seed;
+  fin.seq_id = seq;
+}
+
+sdm_status prefill_impl(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t* d_next_token,
+                        float* d_logits, const Sampling& smp);
+}  // namespace
+
 sdm_status sdm_prefill(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t* d_next_token,
                        float* d_logits) {
+  return prefill_impl(m, seq, d_tokens, n, d_next_token, d_logits, Sampling{});
+}
+
+sdm_status sdm_prefill_sample(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32_t n, float temperature,
+                              uint64_t seed, int32_t* d_next_token, float* d_logits) {
+  Sampling smp;
+  sdm_status s = check_sampling(temperature, seed, &smp);
+  if (s != SDM_OK) return s;
+  return prefill_impl(m, seq, d_tokens, n, d_next_token, d_logits, smp);
+}
+
+namespace {
+sdm_status prefill_impl(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t* d_next_token,
+                        float* d_logits, const Sampling& smp) {
   sdm_status s = check_model(m);
   if (s != SDM_OK) return s;
   if ((s = check_seq(m, seq)) != SDM_OK) return s;
@@ -674,10 +731,12 @@ sdm_status sdm_prefill(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32
     const int T = std::min(C, n - off);
     const bool last = off + T == n;
     FinishArgs fin{};
-    fin.mode = FIN_NEXT;
+    fin.mode = last && smp.on ? FIN_SAMPLE_NEXT : FIN_NEXT;
     fin.slots = one_slot(m, seq, 1);
     fin.T = 1;
     fin.next = d_next_token;
+    fin.target_pos = off + T;
+    set_sampling(fin, smp, seq);
     TokenInput ti;
     ti.tokens = d_tokens + off;
     // intermediate chunks still run the (cheap, one-row) head so that every
@@ -689,8 +748,28 @@ sdm_status sdm_prefill(sdm_model* m, int32_t seq, const int32_t* d_tokens, int32
   q.verified = 0;
   return SDM_OK;
 }
+}  // namespace
+
+namespace {
+sdm_status decode_ar_impl(sdm_model* m, int32_t seq, const int32_t* d_token, int32_t* d_next_token, float* d_logits,
+                          const Sampling& smp);
+}
 
 sdm_status sdm_decode_ar(sdm_model* m, int32_t seq, const int32_t* d_token, int32_t* d_next_token, float* d_logits) {
+  return decode_ar_impl(m, seq, d_token, d_next_token, d_logits, Sampling{});
+}
+
+sdm_status sdm_decode_ar_sample(sdm_model* m, int32_t seq, const int32_t* d_token, float temperature, uint64_t seed,
+                                int32_t* d_next_token, float* d_logits) {
+  Sampling smp;
+  sdm_status s = check_sampling(temperature, seed, &smp);
+  if (s != SDM_OK) return s;
+  return decode_ar_impl(m, seq, d_token, d_next_token, d_logits, smp);
+}
+
+namespace {
+sdm_status decode_ar_impl(sdm_model* m, int32_t seq, const int32_t* d_token, int32_t* d_next_token, float* d_logits,
+                          const Sampling& smp) {
   sdm_status s = check_model(m);
   if (s != SDM_OK) return s;
   if ((s = check_seq(m, seq)) != SDM_OK) return s;
@@ -700,16 +779,19 @@ sdm_status sdm_decode_ar(sdm_model* m, int32_t seq, const int32_t* d_token, int3
   if ((int64_t)q.len + 1 > m->cfg.max_context) return fail(SDM_ERR_CAPACITY, "sequence %d is full", seq);
   if ((s = ensure_pages(m, {seq}, {q.len + 1})) != SDM_OK) return s;
   FinishArgs fin{};
-  fin.mode = FIN_NEXT;
+  fin.mode = smp.on ? FIN_SAMPLE_NEXT : FIN_NEXT;
   fin.slots = one_slot(m, seq, 1);
   fin.T = 1;
   fin.next = d_next_token;
+  fin.target_pos = q.len + 1;
+  set_sampling(fin, smp, seq);
   TokenInput ti;
   ti.tokens = d_token;
   if ((s = forward(m, one_slot(m, seq, 1), CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
   q.verified = 0;
   return set_len(m, seq, q.len + 1);
 }
+}  // namespace
 
 sdm_status sdm_draft_block(sdm_model* m, int32_t seq, const int32_t* d_anchor, int32_t B, int32_t* d_block_out,
                            float* d_logits) {
@@ -754,6 +836,65 @@ sdm_status sdm_verify_block(sdm_model* m, int32_t n_seq, const int32_t* h_seq_id
   ti.tokens = d_block;
   if ((s = forward(m, sl, CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
   for (int32_t id : ids) m->seqs[id].verified = B;
+  return SDM_OK;
+}
+
+sdm_status sdm_draft_block_sample(sdm_model* m, int32_t seq, const int32_t* d_anchor, int32_t B, float temperature,
+                                  uint64_t seed, int32_t* d_block_out, float* d_draft_logits, float* d_draft_stats) {
+  sdm_status s = check_model(m);
+  if (s != SDM_OK) return s;
+  Sampling smp;
+  if ((s = check_sampling(temperature, seed, &smp)) != SDM_OK) return s;
+  if (!d_anchor || !d_block_out || !d_draft_logits || !d_draft_stats) return fail(SDM_ERR_ARG, "null pointer");
+  Slots sl;
+  std::vector<int32_t> ids, ends;
+  if ((s = check_block_call(m, 1, &seq, B, &sl, &ids, &ends)) != SDM_OK) return s;
+  if (B < 2) return fail(SDM_ERR_ARG, "a sampled draft needs B >= 2");
+  if ((s = ensure_pages(m, ids, ends)) != SDM_OK) return s;
+  FinishArgs fin{};
+  fin.mode = FIN_SAMPLE_DRAFT;
+  fin.slots = sl;
+  fin.T = B;
+  fin.anchor = d_anchor;
+  fin.block = d_block_out;
+  fin.draft_stats = d_draft_stats;
+  set_sampling(fin, smp, seq);
+  TokenInput ti;
+  ti.src = TOK_DRAFT;
+  ti.anchor = d_anchor;
+  if ((s = forward(m, sl, BIDIR, ti, false, d_draft_logits, fin)) != SDM_OK) return s;
+  m->seqs[seq].verified = 0;
+  return SDM_OK;
+}
+
+sdm_status sdm_verify_block_sample(sdm_model* m, int32_t seq, const int32_t* d_block, int32_t B, float temperature,
+                                   uint64_t seed, const float* d_draft_logits, const float* d_draft_stats,
+                                   int32_t* d_accept_len, int32_t* d_next_token, float* d_logits) {
+  sdm_status s = check_model(m);
+  if (s != SDM_OK) return s;
+  Sampling smp;
+  if ((s = check_sampling(temperature, seed, &smp)) != SDM_OK) return s;
+  if (!d_block || !d_draft_logits || !d_draft_stats || !d_accept_len || !d_next_token)
+    return fail(SDM_ERR_ARG, "null pointer");
+  Slots sl;
+  std::vector<int32_t> ids, ends;
+  if ((s = check_block_call(m, 1, &seq, B, &sl, &ids, &ends)) != SDM_OK) return s;
+  if (B < 2) return fail(SDM_ERR_ARG, "a sampled verify needs B >= 2");
+  if ((s = ensure_pages(m, ids, ends)) != SDM_OK) return s;
+  FinishArgs fin{};
+  fin.mode = FIN_SAMPLE_VERIFY;
+  fin.slots = sl;
+  fin.T = B;
+  fin.block = (int*)d_block;
+  fin.accept = d_accept_len;
+  fin.next = d_next_token;
+  fin.draft_stats = (float*)d_draft_stats;
+  fin.draft_logits = d_draft_logits;
+  set_sampling(fin, smp, seq);
+  TokenInput ti;
+  ti.tokens = d_block;
+  if ((s = forward(m, sl, CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
+  m->seqs[seq].verified = B;
   return SDM_OK;
 }
 

@@ -164,3 +164,45 @@ def generate_diffusion_batch(model: Model, prompts: Sequence, n_tokens: int, B: 
 def generate_diffusion(model: Model, prompt, n_tokens: int, B: int, tau: float, max_steps: Optional[int] = None,
                        seq: int = 0, tau_revise: Optional[float] = None) -> GpuGen:
     return generate_diffusion_batch(model, [prompt], n_tokens, B, tau, max_steps, [seq], tau_revise)[0]
+
+
+def generate_ar_sample(model: Model, prompt, n_tokens: int, T: float, seed: int, seq: int = 0) -> GpuGen:
+    """AR sampling at temperature T: ``prefill_sample`` then one
+    ``decode_ar_sample`` per token, tokens kept on the device."""
+    dev = model.device
+    out = torch.empty(n_tokens, dtype=torch.int32, device=dev)
+    model.prefill_sample(seq, _ids(prompt, dev), T, seed, out[0:1])
+    base = out.data_ptr()
+    for t in range(1, n_tokens):
+        model.decode_ar_sample(seq, base + 4 * (t - 1), T, seed, base + 4 * t)
+    return GpuGen([int(v) for v in out.cpu().tolist()], n_tokens - 1)
+
+
+def generate_selfspec_sample(model: Model, prompt, n_tokens: int, B: int, T: float, seed: int,
+                             seq: int = 0) -> GpuGen:
+    """Self-speculation at temperature T: ``draft_block_sample`` +
+    ``verify_block_sample`` (rejection-sampling verify) + ``commit_kv(L)``;
+    one 4-byte read of L per cycle."""
+    dev = model.device
+    V = model.shape.vocab
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    model.prefill_sample(seq, _ids(prompt, dev), T, seed, nxt)
+    blk = torch.empty(B, dtype=torch.int32, device=dev)
+    dlog = torch.empty((B, V), dtype=torch.float32, device=dev)
+    dstat = torch.empty((2, B), dtype=torch.float32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    acc_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    toks = [int(nxt.item())]
+    Ls: List[int] = []
+    fw = 0
+    while len(toks) < n_tokens:
+        model.draft_block_sample(seq, nxt, B, T, seed, blk, dlog, dstat)
+        model.verify_block_sample(seq, blk, B, T, seed, dlog, dstat, acc, nxt)
+        acc_host.copy_(acc, non_blocking=True)
+        model.stream.synchronize()
+        L = int(acc_host.item())
+        model.commit_kv(seq, L)
+        toks += blk[1:L].cpu().tolist() + [int(nxt.item())]
+        Ls.append(L)
+        fw += 2
+    return GpuGen(toks[:n_tokens], fw, accept_lengths=Ls)

@@ -176,6 +176,29 @@ class Model:
                   logits: torch.Tensor = None):
         L.check(self.lib.sdm_decode_ar(self.handle, seq, self._addr(token), self._addr(next_token), L.ptr(logits)))
 
+    # -- sampling at temperature > 0 ----------------------------------------------
+    def prefill_sample(self, seq: int, tokens: torch.Tensor, T: float, seed: int, next_token: torch.Tensor,
+                       logits: torch.Tensor = None):
+        L.check(self.lib.sdm_prefill_sample(self.handle, seq, L.ptr(tokens), tokens.numel(), float(T), int(seed),
+                                            L.ptr(next_token), L.ptr(logits)))
+
+    def decode_ar_sample(self, seq: int, token: int | torch.Tensor, T: float, seed: int,
+                         next_token: int | torch.Tensor, logits: torch.Tensor = None):
+        L.check(self.lib.sdm_decode_ar_sample(self.handle, seq, self._addr(token), float(T), int(seed),
+                                              self._addr(next_token), L.ptr(logits)))
+
+    def draft_block_sample(self, seq: int, anchor: int | torch.Tensor, B: int, T: float, seed: int,
+                           block_out: torch.Tensor, draft_logits: torch.Tensor, draft_stats: torch.Tensor):
+        L.check(self.lib.sdm_draft_block_sample(self.handle, seq, self._addr(anchor), B, float(T), int(seed),
+                                                L.ptr(block_out), L.ptr(draft_logits), L.ptr(draft_stats)))
+
+    def verify_block_sample(self, seq: int, block: torch.Tensor, B: int, T: float, seed: int,
+                            draft_logits: torch.Tensor, draft_stats: torch.Tensor, accept_len: torch.Tensor,
+                            next_token: int | torch.Tensor, logits: torch.Tensor = None):
+        L.check(self.lib.sdm_verify_block_sample(self.handle, seq, L.ptr(block), B, float(T), int(seed),
+                                                 L.ptr(draft_logits), L.ptr(draft_stats), L.ptr(accept_len),
+                                                 self._addr(next_token), L.ptr(logits)))
+
     def row_stats(self, tok=None, conf=None, margin=None):
         L.check(self.lib.sdm_row_stats(self.handle, L.ptr(tok), L.ptr(conf), L.ptr(margin)))
 
