@@ -332,6 +332,51 @@ def main() -> int:
             log(f"diffusion S={S}{' revise' if taur is not None else ''}: {diff[key]['ms_per_block']} ms per block, "
                 f"{diff[key]['tok_per_s']} tok/s")
         out["diffusion_step_budget"] = diff
+        # sampling at temperature 1: rejection-sampling self-spec (natural accepts; random weights give
+        # near-uniform rows, so most drafts are accepted) and AR sampling, cycles timed after the prefill
+        V = s.vocab
+        model.seq_reset(1)
+        nxt = torch.empty(1, dtype=torch.int32, device=dev)
+        model.prefill_sample(1, torch.as_tensor(prompt, device=dev), 1.0, 7, nxt)
+        sblk = torch.empty(B, dtype=torch.int32, device=dev)
+        dlog = torch.empty((B, V), dtype=torch.float32, device=dev)
+        dstat = torch.empty((2, B), dtype=torch.float32, device=dev)
+        sacc = torch.empty(1, dtype=torch.int32, device=dev)
+        n_cyc, toks_s, Ls_s, ev_d, ev_v = 24, 0, [], [], []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for c in range(n_cyc):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            model.draft_block_sample(1, nxt, B, 1.0, 7, sblk, dlog, dstat)
+            e[1].record()
+            model.verify_block_sample(1, sblk, B, 1.0, 7, dlog, dstat, sacc, nxt)
+            e[2].record()
+            L = int(sacc.item())
+            model.commit_kv(1, L)
+            Ls_s.append(L)
+            toks_s += L
+            ev_d.append(e)
+        torch.cuda.synchronize()
+        t_ss = time.perf_counter() - t0
+        model.seq_reset(1)
+        abuf = torch.empty(65, dtype=torch.int32, device=dev)
+        model.prefill_sample(1, torch.as_tensor(prompt, device=dev), 1.0, 7, abuf[0:1])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(1, 65):
+            model.decode_ar_sample(1, abuf.data_ptr() + 4 * (t - 1), 1.0, 7, abuf.data_ptr() + 4 * t)
+        torch.cuda.synchronize()
+        t_as = time.perf_counter() - t0
+        out["sampling_T1"] = {
+            "selfspec": {"cycles": n_cyc, "tokens": toks_s, "mean_accept": round(float(np.mean(Ls_s)), 3),
+                         "tok_per_s": round(toks_s / t_ss, 1),
+                         "draft_sample_us": _pct([e[0].elapsed_time(e[1]) * 1e3 for e in ev_d]),
+                         "verify_sample_us": _pct([e[1].elapsed_time(e[2]) * 1e3 for e in ev_d])},
+            "ar": {"tokens": 64, "tok_per_s": round(64 / t_as, 1), "ms_per_token": round(t_as / 64 * 1e3, 3)},
+            "note": "one 4-byte read of L per self-spec cycle (natural accepts); prefill outside the timed region"}
+        log(f"sampling T=1: self-spec {out['sampling_T1']['selfspec']['tok_per_s']} tok/s "
+            f"(mean L {out['sampling_T1']['selfspec']['mean_accept']}), AR {out['sampling_T1']['ar']['tok_per_s']} tok/s")
         out["modes"] = {"selfspec_natural": {"cycles": 16, "tokens": int(sum(Ln)), "tok_per_s": round(sum(Ln) / t_nat, 1),
                                              "mean_accept": round(float(np.mean(Ln)), 3)},
                         "ar": {"tokens": 64, "tok_per_s": round(64 / t_ar, 1), "ms_per_token": round(t_ar / 64 * 1e3, 3)},
