@@ -133,10 +133,12 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   g.MTILES = (rows + 31) / 32;
   g.S = 1;
   if (epi == EPI_PARTIAL) {
-    // enough splits to cover the chip; more while every split still streams
-    // at least 96 k-blocks (long-K matrices), up to four tiles per group
+    // enough splits for two workgroups per compute unit (two waves per SIMD,
+    // so one-tile groups overlap their accumulator chains); more while every
+    // split still streams at least 96 k-blocks (long-K matrices), up to four
+    // tiles per group
     auto ok = [&](int s) { return s <= kMaxSplitK && g.KB % s == 0 && g.KB / s >= 32; };
-    while (g.NT * g.S < kGemmTargetGroups && ok(2 * g.S)) g.S *= 2;
+    while (g.NT * g.S < 2 * kGemmTargetGroups && ok(2 * g.S)) g.S *= 2;
     while (ok(2 * g.S) && g.KB / (2 * g.S) >= 96 && g.NT * 2 * g.S <= 4 * kGemmTargetGroups) g.S *= 2;
   }
   g.WAVES = 4;
