@@ -108,3 +108,18 @@ def test_sampling_argument_errors(small):
             gm.prefill_sample(3, toks, T, 1, nxt)
         assert e.value.status == SDM_ERR_ARG
     assert gm.seq_length(3) == 0                            # nothing ran
+
+
+def test_w4_selfspec_sample_stream():
+    """Sampling on a model with 4-bit decoder weights (the two extensions together)."""
+    from self_speculative_amd import decode as D
+    from self_speculative_amd.model import Model
+    w = W.make_w4_weights(SMALL, seed=41, gains="random")
+    om = O.OracleModel(SMALL, w)
+    gm = Model(SMALL, w, max_seqs=1, max_block=16, max_context=512, max_rows=64)
+    p = W.prompt_ids(SMALL, 50, seed=9)
+    seed, ref = _pick_seed(lambda s: O.generate_selfspec_sample(om, p, 60, 16, 0.9, s), 2e-3, range(1, 12))
+    print(f"w4 self-spec sample seed={seed}: oracle accepts {ref.accept_lengths}", flush=True)
+    g = D.generate_selfspec_sample(gm, p, 60, 16, 0.9, seed, seq=0)
+    gm.close()
+    assert g.tokens == ref.tokens and g.accept_lengths == ref.accept_lengths
