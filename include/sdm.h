@@ -244,7 +244,9 @@ sdm_status sdm_verify_block_sample(sdm_model* m, int32_t seq, const int32_t* d_b
 sdm_status sdm_decode_ar(sdm_model* m, int32_t seq, const int32_t* d_token, int32_t* d_next_token, float* d_logits);
 
 /* Per-row selection of the last forward: token, conf and top-2 margin, each
- * [rows] (nullable).  Device-to-device copies on the model's stream. */
+ * [rows] (nullable).  Device-to-device copies on the model's stream.  After a
+ * sampling call (sdm_*_sample) tok holds the sampled tokens of the rows that
+ * were sampled, and conf and margin are those of the last greedy forward. */
 sdm_status sdm_row_stats(sdm_model* m, int32_t* d_tok, float* d_conf, float* d_margin);
 
 /* Release a sequence's pages and reset it to empty. */
