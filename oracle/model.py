@@ -192,6 +192,30 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, n: int, mode: int,
     return o
 
 
+def attention_masked(q: np.ndarray, K: np.ndarray, V: np.ndarray, vis: np.ndarray,
+                     row_independent: bool = False) -> np.ndarray:
+    """Attention under an explicit visibility.  q [T, Hq, hd]; K, V [nk, Hkv,
+    hd]; vis boolean [T, nk] (row i sees key j iff vis[i, j]).  Returns o [T,
+    Hq, hd]; invisible keys are left out of the softmax."""
+    T, Hq, hd = q.shape
+    Hkv = K.shape[1]
+    scale = 1.0 / math.sqrt(hd)
+    o = np.empty_like(q)
+    for h in range(Hq):
+        kvh = (h * Hkv) // Hq
+        if row_independent:
+            for i in range(T):
+                keys = np.nonzero(vis[i])[0]
+                s = (K[keys, kvh] @ q[i, h]) * scale
+                p = np.exp(s - s.max())
+                o[i, h] = (p @ V[keys, kvh]) / p.sum()
+        else:
+            s = np.where(vis, (q[:, h] @ K[:, kvh].T) * scale, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            o[:, h] = (p @ V[:, kvh]) / p.sum(axis=1, keepdims=True)
+    return o
+
+
 def select_rows(logits: np.ndarray, mask_id: int):
     """Per-row (tok, conf, margin) with MASK excluded.  logits [T, V]."""
     l = np.array(logits, dtype=np.float64, copy=True)
@@ -358,6 +382,43 @@ class OracleModel:
             h = h + self._mm(u, w.wd)
         if logits_rows is not None:
             h = h[np.asarray(logits_rows)]
+        z = self.A(self._norm(h, self.final_norm))
+        return self._mm(z, self.lm_head())
+
+    def forward_masked(self, cache: KVCache, tokens: Sequence[int], positions: Sequence[int],
+                       vis: np.ndarray, n_write: int) -> np.ndarray:
+        """Rows at arbitrary positions under an explicit visibility.
+
+        The keys are the committed prefix 0..n-1 followed by the T rows of
+        this call in row order; ``vis`` [T, n+T] says which of them each row
+        sees.  RoPE uses ``positions``.  The K/V of the first ``n_write`` rows
+        go to the cache's pending rows n..n+n_write-1 (the committed length
+        is not changed); the other rows' K/V live only inside this call.
+        Returns logits [T, V]."""
+        s = self.shape
+        tokens = np.asarray(tokens, dtype=np.int64)
+        pos = np.asarray(positions, dtype=np.int64)
+        T, n = len(tokens), cache.n
+        vis = np.asarray(vis, dtype=bool)
+        assert vis.shape == (T, n + T) and pos.shape == (T,)
+        cache.ensure(n + n_write)
+        cos, sin = rope_tables(pos, s.head_dim, s.rope_base)
+        h = self.embed_rows(tokens)
+        for l in range(s.n_layers):
+            w = self.layer(l)
+            a = self.A(self._norm(h, w.attn_norm))
+            q = self.A(apply_rope(self._mm(a, w.wq).reshape(T, s.n_q_heads, s.head_dim), cos, sin))
+            k = self.R(apply_rope(self._mm(a, w.wk).reshape(T, s.n_kv_heads, s.head_dim), cos, sin))
+            v = self.R(self._mm(a, w.wv).reshape(T, s.n_kv_heads, s.head_dim))
+            cache.K[l][n:n + n_write] = k[:n_write]
+            cache.V[l][n:n + n_write] = v[:n_write]
+            K = np.concatenate([cache.K[l][:n], k])
+            V = np.concatenate([cache.V[l][:n], v])
+            o = attention_masked(q, K, V, vis, self.row_independent)
+            h = h + self._mm(self.A(o.reshape(T, s.q_dim)), w.wo)
+            b = self.A(self._norm(h, w.ffn_norm))
+            u = self.A(silu(self._mm(b, w.wg)) * self._mm(b, w.wu))
+            h = h + self._mm(u, w.wd)
         z = self.A(self._norm(h, self.final_norm))
         return self._mm(z, self.lm_head())
 

@@ -25,6 +25,17 @@ modes as the pages state them:
   classic verify rule).  At temperature 0 the output equals greedy AR
   (fintech-frontier-insights, self-speculation bullet and accuracy list).
 
+* Quadratic self-speculation (a variant the pages name, with a higher
+  tokens-per-forward figure than the linear one: ai-feeds item 3;
+  fintech-frontier-insights, the release summary and its TPF table; no
+  algorithm is given, so this is a reading): one forward verifies the block
+  causally and, in the same pass, drafts the next block for every possible
+  accept length, so no separate draft forward is needed.  The candidate for
+  accept length L = k + 1 is a [MASK x B] block at positions n+k+1..n+k+B
+  that sees the committed prefix, block rows 0..k and, bidirectionally, its
+  own rows; its row 0 sits where the bonus token will go, rows 1..B-1 become
+  the next cycle's drafts behind the AR token a_k.  B + B^2 rows per forward.
+
 Readings of open points (listed in the design notes): the row at a MASK
 position predicts that position in a bidirectional forward, while causal rows
 predict the next position; a self-spec draft is one bidirectional forward over
@@ -182,6 +193,45 @@ class OracleSession:
         return new, U, R, n_left, sel
 
 
+    def verify_block_quadratic(self, seq: int, block: Sequence[int], candidates: Optional[Sequence[int]] = None):
+        """One forward over the block (causal: the verify) and the candidate
+        next blocks.  Candidate k (default: every k in 0..B-1, else the listed
+        ones) is [MASK x B] at positions n+k+1..n+k+B; it sees the committed
+        prefix, block rows 0..k and all of its own rows.  The block's causal
+        K/V go to the pending rows as in ``verify_block``.
+
+        Returns (a, L, nxt, verify rows, {k: candidate rows}): a and L as
+        ``verify_block``; nxt[k] = [a_k, argmax of candidate k's rows 1..B-1],
+        the next cycle's block should L be k + 1 (-1 for candidates left out).
+        """
+        c = self._cache(seq)
+        n = c.n
+        block = np.asarray(block, dtype=np.int32)
+        B = len(block)
+        ks = list(range(B)) if candidates is None else sorted({int(k) for k in candidates})
+        T = B * (1 + len(ks))
+        tokens = np.concatenate([block, np.full(T - B, self.mask_id, dtype=np.int32)])
+        pos = np.concatenate([n + np.arange(B)] + [n + k + 1 + np.arange(B) for k in ks])
+        vis = np.zeros((T, n + T), dtype=bool)
+        vis[:, :n] = True                                        # the committed prefix
+        vis[:B, n:n + B] = np.tril(np.ones((B, B), dtype=bool))  # the verify rows: causal
+        for ci, k in enumerate(ks):
+            r0 = B * (1 + ci)
+            vis[r0:r0 + B, n:n + k + 1] = True                   # block rows 0..k
+            vis[r0:r0 + B, n + r0:n + r0 + B] = True             # its own rows
+        logits = self.model.forward_masked(c, tokens, pos, vis, n_write=B)
+        self.forwards += 1
+        sel = self._sel(logits[:B])
+        a = sel.tok.copy()
+        nxt = np.full((B, B), -1, dtype=np.int32)
+        cands = {}
+        for ci, k in enumerate(ks):
+            cs = self._sel(logits[B * (1 + ci):B * (2 + ci)])
+            cands[k] = cs
+            nxt[k, 0] = a[k]
+            nxt[k, 1:] = cs.tok[1:]
+        return a, accept_length(block, a), nxt, sel, cands
+
     # -- sampling at temperature T > 0 (see oracle/sampling.py) ---------------
     # A sampled token's position is the absolute position it will occupy:
     # prefill of P tokens -> P; an AR step on the token at position n -> n + 1;
@@ -288,6 +338,30 @@ def generate_selfspec(model: OracleModel, prompt: Sequence[int], n_tokens: int, 
         sess.commit_kv(seq, L)
         toks += [int(t) for t in blk[1:L]] + [int(a[L - 1])]
         Ls.append(L)
+        cyc += 1
+    return GenResult(toks[:n_tokens], sess.forwards - 1, accept_lengths=Ls)
+
+
+def generate_selfspec_quadratic(model: OracleModel, prompt: Sequence[int], n_tokens: int, B: int,
+                                forced: Optional[Sequence[int]] = None, seq: int = 0) -> GenResult:
+    """Quadratic self-speculation: a plain draft forward drafts the first
+    block; after that every cycle is one forward that verifies the block and
+    holds the next block for each accept length.  ``forced`` as in
+    ``generate_selfspec``."""
+    sess = OracleSession(model, keep_logits=False)
+    first = sess.prefill(seq, prompt)
+    toks = [int(first.tok[0])]
+    blk, _ = sess.draft_block(seq, toks[-1], B)
+    Ls: List[int] = []
+    cyc = 0
+    while len(toks) < n_tokens:
+        a, L, nxt, _, _ = sess.verify_block_quadratic(seq, blk)
+        if forced is not None:
+            L = int(forced[cyc])
+        sess.commit_kv(seq, L)
+        toks += [int(t) for t in blk[1:L]] + [int(a[L - 1])]
+        Ls.append(L)
+        blk = nxt[L - 1]
         cyc += 1
     return GenResult(toks[:n_tokens], sess.forwards - 1, accept_lengths=Ls)
 
