@@ -196,8 +196,35 @@ sdm_status sdm_draft_block(sdm_model* m, int32_t seq, const int32_t* d_anchor, i
 sdm_status sdm_verify_block(sdm_model* m, int32_t n_seq, const int32_t* h_seq_ids, const int32_t* d_block, int32_t B,
                             int32_t* d_ar_argmax, int32_t* d_accept_len, float* d_logits);
 
+/* Quadratic self-speculation (a variant the pages name with a higher
+ * tokens-per-forward figure than linear self-speculation: ai-feeds item 3;
+ * fintech-frontier-insights, release summary and TPF table; they give no
+ * algorithm, so the rows below are this library's reading).  One forward of
+ * B + B^2 rows on sequence seq (committed length n):
+ *   - the block d_block [B] = [g, d_1..d_{B-1}] at positions n..n+B-1,
+ *     causal: exactly sdm_verify_block's rows, outputs and committable K/V
+ *     (d_ar_argmax [B], d_accept_len [1]);
+ *   - for every k in 0..B-1 a candidate [MASK x B] at positions
+ *     n+k+1..n+k+B that sees keys 0..n+k (the committed prefix and block rows
+ *     0..k) and, bidirectionally, its own rows.  Its K/V stay in the
+ *     workspace and are never committed.
+ * d_next_blocks [B][B] (device, int32): row k = [argmax of block row k (the
+ * token after an accept length of k + 1), argmax of candidate k's rows
+ * 1..B-1] -- the next call's block when the accept length is k + 1, with no
+ * draft forward in between.  d_logits (nullable) [B + B^2][vocab] fp32: the
+ * block's rows then candidate k's rows at B + k*B.  Commit with
+ * sdm_commit_kv(seq, L) as after sdm_verify_block.
+ * Requires 2 <= B <= 63, max_block >= B, max_rows >= B * (B + 1) and
+ * n + 2B <= max_context (SDM_ERR_ARG / SDM_ERR_CAPACITY otherwise).  d_block
+ * must not overlap d_next_blocks (SDM_ERR_ARG).  Calls on one model share the
+ * candidates' workspace, as every call shares the model's workspace. */
+sdm_status sdm_verify_block_quadratic(sdm_model* m, int32_t seq, const int32_t* d_block, int32_t B,
+                                      int32_t* d_ar_argmax, int32_t* d_accept_len, int32_t* d_next_blocks,
+                                      float* d_logits);
+
 /* Commit the first n_accept (1..B of the last verify) positions of the last
- * causal block forward of seq.  Requires a preceding sdm_verify_block on seq. */
+ * causal block forward of seq.  Requires a preceding sdm_verify_block (or
+ * sdm_verify_block_quadratic, or sampled verify) on seq. */
 sdm_status sdm_commit_kv(sdm_model* m, int32_t seq, int32_t n_accept);
 
 /* Sampling at temperature > 0 (one sequence per call).  The pages state the

@@ -66,6 +66,8 @@ SIGNATURES = {
     "sdm_verify_block_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_float, c_uint64, c_void_p,
                                           c_void_p, c_void_p, c_void_p, c_void_p]),
     "sdm_draft_block": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+    "sdm_verify_block_quadratic": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                             c_void_p]),
     "sdm_verify_block": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_int32, c_void_p, c_void_p,
                                    c_void_p]),
     "sdm_commit_kv": (c_int32, [c_void_p, c_int32, c_int32]),

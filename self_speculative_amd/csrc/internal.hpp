@@ -17,7 +17,10 @@ constexpr int kAttnStagedPairs = 256;  // (split, KV head) pairs from which atte
 enum Mode { CAUSAL = 0, BIDIR = 1 };
 enum Epi { EPI_QKV = 0, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 enum Finish { FIN_NEXT = 0, FIN_DRAFT = 1, FIN_VERIFY = 2, FIN_DIFFUSE = 3,
-              FIN_SAMPLE_NEXT = 4, FIN_SAMPLE_DRAFT = 5, FIN_SAMPLE_VERIFY = 6 };
+              FIN_SAMPLE_NEXT = 4, FIN_SAMPLE_DRAFT = 5, FIN_SAMPLE_VERIFY = 6, FIN_QUAD = 7 };
+__host__ __device__ inline bool is_sampling(int fin_mode) {
+  return fin_mode >= FIN_SAMPLE_NEXT && fin_mode <= FIN_SAMPLE_VERIFY;
+}
 // Random-number purposes of the sampling modes (counter word 3).
 enum Purpose { PURPOSE_DRAFT = 1, PURPOSE_ACCEPT = 2, PURPOSE_RESIDUAL = 3, PURPOSE_SAMPLE = 4 };
 constexpr int kSampleParts = 64;  // workgroups sharing one row's vocabulary when sampling
@@ -28,7 +31,9 @@ struct SamplePart {
   float best, second, m, s;
   int idx, pad0, pad1, pad2;
 };
-enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1 };
+// Token source of the embedding: the given ids; [anchor, MASK...] per slot;
+// the given T ids then MASK for every later row (quadratic self-speculation).
+enum TokSrc { TOK_PLAIN = 0, TOK_DRAFT = 1, TOK_QUAD = 2 };
 
 // Activations of the bf16 path travel between kernels as two bf16 planes, hi
 // and lo, with value hi + lo: hi = RNE_bf16(x), lo = RNE_bf16(x - hi) (a
@@ -66,12 +71,28 @@ __host__ __device__ inline int kv_v_index(int pk, int d) {
   return ((((d >> 5) * (kPageTokens / 16) + (pk >> 4)) * 64 + lane) << 3) + e;
 }
 
+// Candidate slots (quadratic self-speculation): when xslot0 > 0, every slot
+// s >= xslot0 is a candidate block.  Its rows sit at positions len[s] + t and
+// see keys [0, len[s]) of its sequence's pages plus, bidirectionally, its own
+// T rows, whose K/V live in the scratch page (s - xslot0) of KvView::xpool
+// (key t at page position t) instead of the sequence's pages.
 struct Slots {
   int n_seq;   // sequences in this forward
   int T;       // rows per sequence
   int ids[kMaxSlots];
   int len[kMaxSlots];  // committed length per slot: the block's first position
+  int xslot0;          // first candidate slot; 0: none
 };
+__host__ __device__ inline bool is_candidate(const Slots& s, int slot) { return s.xslot0 > 0 && slot >= s.xslot0; }
+
+// Attention splits of one slot: its keys in the sequence's pages in ranges of
+// kAttnSplitKeys, then, for a candidate, one more split over its own block.
+constexpr int kMaxSplits = 256;  // splits the combine kernel merges per (slot, KV head)
+__host__ __device__ inline int attn_splits(const Slots& s, int slot) {
+  const bool c = is_candidate(s, slot);
+  const int paged = c ? s.len[slot] : s.len[slot] + s.T;
+  return (paged + kAttnSplitKeys - 1) / kAttnSplitKeys + (c ? 1 : 0);
+}
 
 struct KvView {
   void* pool;            // page base
@@ -80,6 +101,8 @@ struct KvView {
   const int* page_table; // [max_seqs][max_pages]
   int max_pages;
   int Hkv, hd;
+  void* xpool;           // candidate slots' own K/V: pages of one layer, x_page_elems apart
+  int64_t x_page_elems;
 };
 
 struct EpiArgs {
@@ -257,6 +280,7 @@ struct FinishArgs {
   float* draft_stats;    // DRAFT out / VERIFY in: [2][T] ln q(d_t), lse of draft row t
   const float* draft_logits;  // VERIFY: the draft forward's logits [T][V]
   int* next;             // NEXT: device token (last row of slot 0)
+  int* next_blocks;      // QUAD: [T][T], row k = [a_k, candidate k's argmax at rows 1..T-1]
 };
 
 // Kernel timing: when set, the next launch carries these events on its own

@@ -109,6 +109,7 @@ __global__ void k_embed(const T* __restrict__ E, int d, int V, const int* __rest
   const int m = blockIdx.x;
   int tok;
   if (tok_src == TOK_DRAFT) tok = (m % T_ == 0) ? anchor[m / T_] : mask_id;
+  else if (tok_src == TOK_QUAD) tok = m < T_ ? tokens[m] : mask_id;
   else tok = tokens[m];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // out-of-range ids are clamped, never read out of bounds
   for (int k = threadIdx.x; k < d; k += blockDim.x) x[(int64_t)m * d + k] = load_as_f32<T>(E, (int64_t)tok * d + k);
@@ -285,7 +286,8 @@ __device__ __forceinline__ void epi_preload(EpiPre& p, int nt, int mt, int lane,
     const int slot = m / ea.slots.T, t = m % ea.slots.T;
     const int seq = ea.slots.ids[slot];
     p.pos = ea.slots.len[slot] + t;
-    p.page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + p.pos / kPageTokens];
+    p.page = is_candidate(ea.slots, slot) ? -1 - (slot - ea.slots.xslot0)  // scratch page of the candidate
+                                          : ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + p.pos / kPageTokens];
     const int head = nt >> 2, s4 = nt & 3;
     if (head < ea.Hq + ea.kv.Hkv) {
 #pragma unroll
@@ -312,12 +314,15 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
     const int pos = pre.pos;
     const int head = nt >> 2, s4 = nt & 3;
     const int Hq = ea.Hq, Hkv = ea.kv.Hkv;
-    uint16_t* pool = (uint16_t*)ea.kv.pool;
-    const int pk = pos % kPageTokens;
+    // a candidate slot's K/V go to its scratch page, key t at page position t
+    const bool own = pre.page < 0;
+    uint16_t* pool = own ? (uint16_t*)ea.kv.xpool : (uint16_t*)ea.kv.pool;
+    const int pk = own ? m % ea.slots.T : pos % kPageTokens;
     uint16_t* kblk = nullptr;
     uint16_t* vblk = nullptr;
     if (head >= Hq) {
-      const int64_t base = (int64_t)pre.page * ea.kv.page_elems + ea.kv.layer_off;
+      const int64_t base = own ? (int64_t)(-1 - pre.page) * ea.kv.x_page_elems
+                               : (int64_t)pre.page * ea.kv.page_elems + ea.kv.layer_off;
       if (head < Hq + Hkv) kblk = pool + base + (int64_t)(head - Hq) * kPageTokens * kHd;
       else vblk = pool + base + (int64_t)(Hkv + head - Hq - Hkv) * kPageTokens * kHd;
     }
@@ -957,6 +962,31 @@ __device__ __forceinline__ const uint16_t* attn_page_base(const AttnArgs& a, int
   return (const uint16_t*)a.kv.pool + (int64_t)page * a.kv.page_elems + a.kv.layer_off;
 }
 
+// The keys of split sp of a slot.  A plain slot's splits cover keys
+// [0, n + T) of its pages, those below n visible to every row and the block's
+// by the mode.  A candidate slot's splits cover keys [0, n) of its pages, all
+// visible, then one split over its own block in its scratch page (keys
+// 0..T-1, all visible).  Wave w's page starts at key jw; keys [jw, jend)
+// exist; keys below jall are visible to every row.
+struct AttnKeys {
+  bool own;
+  int jend, jall, split0;  // split0: first key of the split
+};
+__device__ __forceinline__ AttnKeys attn_keys(const AttnArgs& a, int slot, int n, int T, int sp, int nsp) {
+  AttnKeys k;
+  const bool cand = is_candidate(a.slots, slot);
+  k.own = cand && sp == nsp - 1;
+  k.jend = k.own ? T : (cand ? n : n + T);
+  k.jall = cand ? k.jend : n;
+  k.split0 = k.own ? 0 : sp * kAttnSplitKeys;
+  return k;
+}
+__device__ __forceinline__ const uint16_t* attn_keys_base(const AttnArgs& a, const AttnKeys& k, int slot, int seq,
+                                                          int jw) {
+  if (k.own) return (const uint16_t*)a.kv.xpool + (int64_t)(slot - a.slots.xslot0) * a.kv.x_page_elems;
+  return attn_page_base(a, seq, jw);
+}
+
 // Grid: linear id -> (pair = split * Hkv + g, query tile); workgroups sharing
 // a pair get linear ids congruent mod 8 so that they are placed on the same
 // XCD and share its L2 for the K/V pages.
@@ -969,23 +999,23 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int seq = a.slots.ids[slot];
   const int T = a.slots.T;
   const int n = a.slots.len[slot];
-  const int nkeys = n + T;
   const int Hkv = a.kv.Hkv;
   const int G = a.Hq / Hkv;
   const int nq = G * T;
   const int nqt = (nq + 31) >> 5;
-  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  const int nsp = attn_splits(a.slots, slot);
   const int L = blockIdx.x;
   const int qt = (L % (8 * nqt)) / 8;
   const int pair = (L / (8 * nqt)) * 8 + (L % 8);
   if (pair >= nsp * Hkv) return;
   const int sp = pair / Hkv, g = pair % Hkv;
-  const int jw = sp * kAttnSplitKeys + 64 * wave;  // this wave's page of keys
+  const AttnKeys ks = attn_keys(a, slot, n, T, sp, nsp);
+  const int jw = ks.split0 + 64 * wave;  // this wave's page of keys
 
   // K and V page blocks of head g for this wave's keys: 16 + 16 vectors per lane
   u32x4 kv_k[16], kv_v[16];
-  if (jw < nkeys) {
-    const uint16_t* pb = attn_page_base(a, seq, jw);
+  if (jw < ks.jend) {
+    const uint16_t* pb = attn_keys_base(a, ks, slot, seq, jw);
     const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
     const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
 #pragma unroll
@@ -999,8 +1029,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   u32x4 qop[8], qlo[QLO ? 8 : 1];
   attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
   AttnState st;
-  attn_page_state<QLO>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, nkeys, n,
-                       n + t, cval, h, st);
+  attn_page_state<QLO>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, ks.jend,
+                       ks.jall, n + t, cval, h, st);
   // the page states meet in LDS; per column, merged in page order
   if (h == 0) {
     s_ml[wave][0][lane & 31] = st.m;
@@ -1047,19 +1077,19 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
   const int seq = a.slots.ids[slot];
   const int T = a.slots.T;
   const int n = a.slots.len[slot];
-  const int nkeys = n + T;
   const int Hkv = a.kv.Hkv;
   const int G = a.Hq / Hkv;
   const int nq = G * T;
   const int nqt = (nq + 31) >> 5;
-  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  const int nsp = attn_splits(a.slots, slot);
   const int pair = blockIdx.x;
   if (pair >= nsp * Hkv) return;
   const int sp = pair / Hkv, g = pair % Hkv;
+  const AttnKeys ks = attn_keys(a, slot, n, T, sp, nsp);
   {
-    const int jw = sp * kAttnSplitKeys + 64 * wave;  // wave w stages page w
-    if (jw < nkeys) {
-      const uint16_t* pb = attn_page_base(a, seq, jw);
+    const int jw = ks.split0 + 64 * wave;  // wave w stages page w
+    if (jw < ks.jend) {
+      const uint16_t* pb = attn_keys_base(a, ks, slot, seq, jw);
       const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
       const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
       u32x4 tk[16], tv[16];
@@ -1084,7 +1114,7 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
     // page 0 starts the running state, pages 1..3 merge into it in order
 #pragma unroll 1
     for (int w = 0; w < 4; ++w) {
-      const int jw = sp * kAttnSplitKeys + 64 * w;
+      const int jw = ks.split0 + 64 * w;
       AttnState& st = w == 0 ? run : pg;
       // the page's 32 operand tiles come out of LDS in one burst
       u32x4 pk[16], pv[16];
@@ -1092,8 +1122,8 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
       for (int i = 0; i < 16; ++i) pk[i] = s_k[w][i][lane];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i] = s_v[w][i][lane];
-      attn_page_state<QLO>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, nkeys, n,
-                           n + t, cval, h, st);
+      attn_page_state<QLO>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, ks.jend,
+                           ks.jall, n + t, cval, h, st);
       if (w > 0) {
         float M, ca, cb;
         attn_merge_coef(run.m, pg.m, M, ca, cb);
@@ -1126,8 +1156,6 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
 // The splits' (m, l) go to LDS with all 256 threads loading, the weights are
 // formed there, then every thread sums two (dim, column) outputs with its
 // partial-O loads issued 8 splits at a time.
-constexpr int kMaxSplits = 256;  // 65536 keys
-
 __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
   __shared__ float s_m[kMaxSplits][32];
   __shared__ float s_l[kMaxSplits][32];
@@ -1135,8 +1163,7 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
   const int ct = blockIdx.x, dch = blockIdx.y % (kHd / 16), g = blockIdx.y / (kHd / 16), slot = blockIdx.z;
   const int T = a.slots.T;
   const int Hkv = a.kv.Hkv, G = a.Hq / Hkv, nq = G * T;
-  const int nkeys = a.slots.len[slot] + T;
-  const int nsp = (nkeys + kAttnSplitKeys - 1) / kAttnSplitKeys;
+  const int nsp = attn_splits(a.slots, slot);
   const int64_t b0 = ((int64_t)slot * Hkv + g) * a.max_splits;
   const int col = threadIdx.x & 31, row = threadIdx.x >> 5;
   const int c = ct * 32 + col;
@@ -1293,11 +1320,16 @@ __global__ void k_finish_mode(FinishArgs f) {
   } else if (f.mode == FIN_DRAFT) {
     f.block[r0] = f.anchor[slot];
     for (int j = 1; j < T; ++j) f.block[r0 + j] = f.tok[r0 + j];
-  } else if (f.mode == FIN_VERIFY) {
+  } else if (f.mode == FIN_VERIFY || (f.mode == FIN_QUAD && slot == 0)) {
     int k = 0;
     while (k + 1 <= T - 1 && f.block[r0 + k + 1] == f.tok[r0 + k]) ++k;
     for (int j = 0; j < T; ++j) f.ar_out[r0 + j] = f.tok[r0 + j];
     f.accept[slot] = k + 1;
+  } else if (f.mode == FIN_QUAD) {
+    // candidate k = slot - 1: the next block should the accept length be k + 1
+    const int k = slot - 1;
+    f.next_blocks[k * T] = f.tok[k];
+    for (int j = 1; j < T; ++j) f.next_blocks[k * T + j] = f.tok[r0 + j];
   } else {  // FIN_DIFFUSE
     // masked positions: the unmask rule; written positions: the revise rule
     // (tau_revise >= 1 never fires, conf <= 1).  Each decision reads only its
@@ -1551,7 +1583,7 @@ static hipError_t launch_finish_sample(const FinishArgs& f, hipStream_t st) {
 }
 
 hipError_t launch_finish(const FinishArgs& f, hipStream_t st) {
-  if (f.mode >= FIN_SAMPLE_NEXT) return launch_finish_sample(f, st);
+  if (is_sampling(f.mode)) return launch_finish_sample(f, st);
   SDM_LAUNCH(k_select_rows, dim3(f.M), dim3(256), 0, st, f.records, f.n_vtiles, f.tok, f.conf, f.margin);
   SDM_LAUNCH(k_finish_mode, dim3(f.slots.n_seq), dim3(64), 0, st, f);
   return hipGetLastError();
@@ -1584,10 +1616,14 @@ __global__ void k_qkv_post_f32(const float* __restrict__ Y, EpiArgs ea, int hd) 
   const int slot = m / ea.slots.T, t = m % ea.slots.T;
   const int seq = ea.slots.ids[slot];
   const int pos = ea.slots.len[slot] + t;
-  const int page = ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + pos / kPageTokens];
-  const int pk = pos % kPageTokens;
-  float* pool = (float*)ea.kv.pool;
-  const int64_t pbase = (int64_t)page * ea.kv.page_elems + ea.kv.layer_off;
+  // a candidate slot's K/V go to its scratch page, key t at page position t
+  const bool own = is_candidate(ea.slots, slot);
+  const int pk = own ? t : pos % kPageTokens;
+  float* pool = own ? (float*)ea.kv.xpool : (float*)ea.kv.pool;
+  const int64_t pbase =
+      own ? (int64_t)(slot - ea.slots.xslot0) * ea.kv.x_page_elems
+          : (int64_t)ea.kv.page_table[(int64_t)seq * ea.kv.max_pages + pos / kPageTokens] * ea.kv.page_elems +
+                ea.kv.layer_off;
   const float* y = Y + (int64_t)m * ncols;
   for (int i = threadIdx.x; i < (Hq + 2 * Hkv) * half; i += blockDim.x) {
     const int head = i / half, dl = i % half;
@@ -1615,7 +1651,9 @@ hipError_t launch_qkv_post_f32(const float* Y, const EpiArgs& ea, int hd, hipStr
   return hipGetLastError();
 }
 
-// One thread per (row, q head); keys visited in ascending order.
+// One thread per (row, q head); keys visited in ascending order.  A
+// candidate slot's visible keys are [0, n) of its pages, then its own block in
+// its scratch page.
 __global__ void k_attn_f32(const float* __restrict__ q, KvView kv, Slots sl, int Hq, int mode,
                            float* __restrict__ out) {
   const int m = blockIdx.x;
@@ -1626,15 +1664,25 @@ __global__ void k_attn_f32(const float* __restrict__ q, KvView kv, Slots sl, int
   const int slot = m / sl.T, t = m % sl.T;
   const int seq = sl.ids[slot];
   const int n = sl.len[slot];
-  const int last = (mode == BIDIR) ? n + sl.T - 1 : n + t;
+  const bool cand = is_candidate(sl, slot);
+  const int npaged = cand ? n : ((mode == BIDIR) ? n + sl.T : n + t + 1);  // visible keys in the pages
+  const int nvis = npaged + (cand ? sl.T : 0);
   const float* pool = (const float*)kv.pool;
+  const float* own = cand ? (const float*)kv.xpool + (int64_t)(slot - sl.xslot0) * kv.x_page_elems : nullptr;
   const int* ptab = kv.page_table + (int64_t)seq * kv.max_pages;
+  // element offset of key j's row of K head g (V: + Hkv * kPageTokens * hd) in its page
+  auto key_row = [&](int j) -> const float* {
+    if (j < npaged)
+      return pool + (int64_t)ptab[j / kPageTokens] * kv.page_elems + kv.layer_off +
+             ((int64_t)g * kPageTokens + j % kPageTokens) * hd;
+    return own + ((int64_t)g * kPageTokens + (j - npaged)) * hd;
+  };
+  const int64_t vofs = (int64_t)Hkv * kPageTokens * hd;
   const float* qv = q + ((int64_t)m * Hq + head) * hd;
   const float scale = 1.f / sqrtf((float)hd);
   float mx = -INFINITY;
-  for (int j = 0; j <= last; ++j) {
-    const float* kr = pool + (int64_t)ptab[j / kPageTokens] * kv.page_elems + kv.layer_off +
-                      ((int64_t)g * kPageTokens + j % kPageTokens) * hd;
+  for (int j = 0; j < nvis; ++j) {
+    const float* kr = key_row(j);
     float s = 0.f;
     for (int d = 0; d < hd; ++d) s = fmaf(qv[d], kr[d], s);
     mx = fmaxf(mx, s * scale);
@@ -1642,10 +1690,9 @@ __global__ void k_attn_f32(const float* __restrict__ q, KvView kv, Slots sl, int
   float acc[128];
   for (int d = 0; d < hd; ++d) acc[d] = 0.f;
   float sum = 0.f;
-  for (int j = 0; j <= last; ++j) {
-    const int64_t pb = (int64_t)ptab[j / kPageTokens] * kv.page_elems + kv.layer_off;
-    const float* kr = pool + pb + ((int64_t)g * kPageTokens + j % kPageTokens) * hd;
-    const float* vr = pool + pb + ((int64_t)(Hkv + g) * kPageTokens + j % kPageTokens) * hd;
+  for (int j = 0; j < nvis; ++j) {
+    const float* kr = key_row(j);
+    const float* vr = kr + vofs;
     float s = 0.f;
     for (int d = 0; d < hd; ++d) s = fmaf(qv[d], kr[d], s);
     const float p = expf(s * scale - mx);

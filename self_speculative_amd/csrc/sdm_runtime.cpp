@@ -71,6 +71,8 @@ sdm_status check_config(const sdm_config* c) {
 struct Dims {
   int L, d, Hq, Hkv, hd, F, V, G, qkv, qd;
   int R, R32, max_pages, max_splits, max_slots, nq_cap;
+  int x_cap;             // largest block of quadratic self-speculation (B + B^2 rows); 0: none
+  int64_t x_page_elems;  // one candidate's scratch page (one layer)
   bool bf16;
   bool w4;  // decoder matrices are 4-bit
   int64_t elt;
@@ -85,8 +87,13 @@ Dims dims_of(const sdm_config* c) {
   D.F = c->ffn_dim; D.V = c->vocab; D.G = D.Hq / D.Hkv; D.qd = D.Hq * D.hd; D.qkv = D.qd + 2 * D.Hkv * D.hd;
   D.R = c->max_rows; D.R32 = (int)align_up(D.R, 32);
   D.max_pages = (int)pages_for(c->max_context, kPageTokens);
-  D.max_splits = (c->max_context + kAttnSplitKeys - 1) / kAttnSplitKeys;
-  D.max_slots = std::min(c->max_seqs, kMaxSlots);
+  // one more split than the context needs: a candidate block's own keys
+  D.max_splits = (c->max_context + kAttnSplitKeys - 1) / kAttnSplitKeys + 1;
+  D.x_cap = 0;
+  for (int b = 2; b <= std::min({c->max_block, kPageTokens, kMaxSlots - 1}); ++b)
+    if ((int64_t)b * (b + 1) <= c->max_rows) D.x_cap = b;
+  D.x_page_elems = 2LL * D.Hkv * kPageTokens * D.hd;
+  D.max_slots = std::max(std::min(c->max_seqs, kMaxSlots), D.x_cap ? D.x_cap + 1 : 0);
   D.nq_cap = D.G * D.R + 32 * D.max_slots;
   D.bf16 = c->dtype == SDM_BF16;
   D.w4 = D.bf16 && c->weight_format == SDM_WEIGHTS_INT4;
@@ -102,7 +109,7 @@ Dims dims_of(const sdm_config* c) {
 
 struct Layout {
   int64_t x, xn, q, attn, hbuf, ybuf, part, opart, mlpart, records, tok, conf, margin, rope_cos, rope_sin,
-      page_table, slog, sparts, slse, sgap, slogp, sprobe, total;
+      page_table, slog, sparts, slse, sgap, slogp, sprobe, xkv, total;
 };
 
 Layout layout_of(const sdm_config* c) {
@@ -147,6 +154,8 @@ Layout layout_of(const sdm_config* c) {
   Lo.sgap = take((int64_t)D.R * 4);
   Lo.slogp = take((int64_t)D.R * 4);
   Lo.sprobe = take((int64_t)D.R * 4);
+  // quadratic self-speculation: each candidate block's K/V of the current layer
+  Lo.xkv = take((int64_t)D.x_cap * D.x_page_elems * D.elt);
   Lo.total = off;
   return Lo;
 }
@@ -269,6 +278,8 @@ KvView kv_view(const sdm_model* m, int layer) {
   kv.max_pages = m->D.max_pages;
   kv.Hkv = m->D.Hkv;
   kv.hd = m->D.hd;
+  kv.xpool = m->ws + m->lo.xkv;
+  kv.x_page_elems = m->D.x_page_elems;
   return kv;
 }
 
@@ -361,8 +372,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
       aa.out_packed = 1;
       aa.out_plane = D.attn_plane;
       int grid_splits = 0;
-      for (int i = 0; i < sl.n_seq; ++i)
-        grid_splits = std::max(grid_splits, (m->seqs[sl.ids[i]].len + sl.T + kAttnSplitKeys - 1) / kAttnSplitKeys);
+      for (int i = 0; i < sl.n_seq; ++i) grid_splits = std::max(grid_splits, attn_splits(sl, i));
       { TimedScope ts(m, SDM_K_ATTN);
         HIP_TRY(launch_attention_bf16(aa, grid_splits, st), "attention"); }
       { TimedScope ts(m, SDM_K_ATTN_COMBINE);
@@ -408,7 +418,7 @@ sdm_status forward_body(sdm_model* m, const Slots& sl, int mode, const TokenInpu
           "final rmsnorm");
   ea.M = ML;
   ea.logits = d_logits;
-  const bool sampling = fin.mode >= FIN_SAMPLE_NEXT;
+  const bool sampling = is_sampling(fin.mode);
   if (sampling && D.bf16 && !d_logits) ea.logits = m->at<float>(m->lo.slog);
   if (D.bf16) {
     TimedScope ts(m, SDM_K_LM_HEAD);
@@ -611,6 +621,9 @@ sdm_status sdm_init_model(const sdm_config* cfg, const sdm_weights* w, void* kv_
   // finite values (their probabilities are exactly 0), so the pool starts zeroed.
   if (e == hipSuccess)
     e = hipMemsetAsync(kv_pool, 0, (size_t)n_pages * (size_t)(m->page_elems * m->D.elt), m->stream);
+  // likewise the candidate blocks' scratch pages (keys past B are never written)
+  if (e == hipSuccess && m->D.x_cap)
+    e = hipMemsetAsync(m->ws + lo.xkv, 0, (size_t)(m->D.x_cap * m->D.x_page_elems * m->D.elt), m->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
   if (e != hipSuccess) {
     delete m;
@@ -836,6 +849,52 @@ sdm_status sdm_verify_block(sdm_model* m, int32_t n_seq, const int32_t* h_seq_id
   ti.tokens = d_block;
   if ((s = forward(m, sl, CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
   for (int32_t id : ids) m->seqs[id].verified = B;
+  return SDM_OK;
+}
+
+sdm_status sdm_verify_block_quadratic(sdm_model* m, int32_t seq, const int32_t* d_block, int32_t B,
+                                      int32_t* d_ar_argmax, int32_t* d_accept_len, int32_t* d_next_blocks,
+                                      float* d_logits) {
+  sdm_status s = check_model(m);
+  if (s != SDM_OK) return s;
+  if (!d_block || !d_ar_argmax || !d_accept_len || !d_next_blocks) return fail(SDM_ERR_ARG, "null pointer");
+  if (d_block + B > d_next_blocks && d_block < d_next_blocks + (int64_t)B * B)
+    return fail(SDM_ERR_ARG, "d_block overlaps d_next_blocks");
+  Slots sl;
+  std::vector<int32_t> ids, ends;
+  if ((s = check_block_call(m, 1, &seq, B, &sl, &ids, &ends)) != SDM_OK) return s;
+  if (B < 2) return fail(SDM_ERR_ARG, "quadratic self-speculation needs B >= 2");
+  if (B > m->D.x_cap)
+    return fail(SDM_ERR_CAPACITY, "block %d needs max_rows >= B * (B + 1) = %d and max_block >= B (largest here: %d)",
+                B, B * (B + 1), m->D.x_cap);
+  const int32_t n = m->seqs[seq].len;
+  if ((int64_t)n + 2 * B > m->cfg.max_context)
+    return fail(SDM_ERR_CAPACITY, "candidate blocks would reach past max_context");
+  // the block (slot 0, causal) and candidate k at slot 1 + k, positions n+k+1..n+k+B
+  sl.n_seq = 1 + B;
+  sl.xslot0 = 1;
+  for (int k = 0; k < B; ++k) {
+    sl.ids[1 + k] = seq;
+    sl.len[1 + k] = n + k + 1;
+  }
+  if (m->D.bf16 && (int64_t)(1 + B) * align_up((int64_t)m->D.G * B, 32) > m->D.nq_cap)
+    return fail(SDM_ERR_CAPACITY, "attention workspace too small for the candidate blocks");
+  if (attn_splits(sl, B) > std::min(kMaxSplits, m->D.max_splits))
+    return fail(SDM_ERR_CAPACITY, "context too long for quadratic self-speculation");
+  if ((s = ensure_pages(m, ids, ends)) != SDM_OK) return s;
+  FinishArgs fin{};
+  fin.mode = FIN_QUAD;
+  fin.slots = sl;
+  fin.T = B;
+  fin.block = (int*)d_block;
+  fin.ar_out = d_ar_argmax;
+  fin.accept = d_accept_len;
+  fin.next_blocks = d_next_blocks;
+  TokenInput ti;
+  ti.tokens = d_block;
+  ti.src = TOK_QUAD;
+  if ((s = forward(m, sl, CAUSAL, ti, false, d_logits, fin)) != SDM_OK) return s;
+  m->seqs[seq].verified = B;
   return SDM_OK;
 }
 

@@ -6,6 +6,10 @@
   [anchor, MASK x (B-1)]), ``verify_block`` (causal forward), ``commit_kv(L)``.
   With a forced accept-length schedule the host knows L in advance and the
   loop never synchronises; with the natural L one 4-byte read per cycle.
+* ``generate_selfspec_quadratic``: one ``draft_block`` for the first block,
+  then per cycle one ``verify_block_quadratic`` (the verify plus a candidate
+  next block for every accept length) and ``commit_kv(L)``; the next block is
+  row L-1 of the cycle's output, passed by address.
 * ``generate_diffusion``: per block, ``diffuse_step`` until no MASK is left
   (step ``max_steps``-1 unmasks everything), then ``verify_block`` +
   ``commit_kv(B)`` commit the block's causal K/V.  Several sequences step in
@@ -105,6 +109,62 @@ def generate_selfspec(model: Model, prompt, n_tokens: int, B: int, forced: Optio
     for c, L in enumerate(Ls):
         toks += [int(t) for t in bl[c, 1:L]] + [int(ar[c, L - 1])]
     return GpuGen(toks[:n_tokens], 2 * len(Ls), accept_lengths=Ls)
+
+
+class QuadSpecRun:
+    """Quadratic self-speculation with per-cycle device outputs: cycle c
+    writes ar[c], the accept length and nexts[c] [B][B]; the block of cycle
+    c + 1 is row L - 1 of nexts[c]."""
+
+    def __init__(self, model: Model, B: int, seq: int, n_cycles: int):
+        self.m, self.B, self.seq = model, B, seq
+        dev = model.device
+        self.first_block = torch.empty(B, dtype=torch.int32, device=dev)
+        self.ars = torch.empty((n_cycles, B), dtype=torch.int32, device=dev)
+        self.nexts = torch.empty((n_cycles, B, B), dtype=torch.int32, device=dev)
+        self.acc = torch.empty(1, dtype=torch.int32, device=dev)
+        self.acc_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+        self.block_addr = self.first_block.data_ptr()
+
+    def draft_first(self, anchor_addr: int):
+        self.m.draft_block(self.seq, anchor_addr, self.B, self.first_block)
+        self.block_addr = self.first_block.data_ptr()
+
+    def cycle(self, c: int, forced_L: Optional[int]) -> int:
+        """One quadratic forward + commit.  Returns L (host value); for natural
+        L this synchronises on a 4-byte copy."""
+        m = self.m
+        m.verify_block_quadratic(self.seq, self.block_addr, self.B, self.ars[c], self.acc, self.nexts[c])
+        if forced_L is None:
+            self.acc_host.copy_(self.acc, non_blocking=True)
+            m.stream.synchronize()
+            L = int(self.acc_host[0])
+        else:
+            L = int(forced_L)
+        m.commit_kv(self.seq, L)
+        self.block_addr = self.nexts[c].data_ptr() + 4 * self.B * (L - 1)
+        return L
+
+
+def generate_selfspec_quadratic(model: Model, prompt, n_tokens: int, B: int,
+                                forced: Optional[Sequence[int]] = None, seq: int = 0) -> GpuGen:
+    first = prefill(model, seq, prompt)
+    run = QuadSpecRun(model, B, seq, n_tokens)
+    run.draft_first(first.data_ptr())
+    Ls: List[int] = []
+    emitted = 1
+    while emitted < n_tokens:
+        L = run.cycle(len(Ls), None if forced is None else forced[len(Ls)])
+        Ls.append(L)
+        emitted += L
+    ar = run.ars[: len(Ls)].cpu().numpy()
+    nx = run.nexts[: len(Ls)].cpu().numpy()
+    blk = run.first_block.cpu().numpy()
+    toks = [int(first.item())]
+    for c, L in enumerate(Ls):
+        toks += [int(t) for t in blk[1:L]] + [int(ar[c, L - 1])]
+        blk = nx[c, L - 1]
+    return GpuGen(toks[:n_tokens], 1 + len(Ls), accept_lengths=Ls)
 
 
 def generate_diffusion_batch(model: Model, prompts: Sequence, n_tokens: int, B: int, tau: float,

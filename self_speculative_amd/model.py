@@ -169,6 +169,11 @@ class Model:
         L.check(self.lib.sdm_verify_block(self.handle, len(seq_ids), ids, self._addr(block), B, L.ptr(ar_argmax),
                                           L.ptr(accept_len), L.ptr(logits)))
 
+    def verify_block_quadratic(self, seq: int, block: int | torch.Tensor, B: int, ar_argmax: torch.Tensor,
+                               accept_len: torch.Tensor, next_blocks: torch.Tensor, logits: torch.Tensor = None):
+        L.check(self.lib.sdm_verify_block_quadratic(self.handle, seq, self._addr(block), B, L.ptr(ar_argmax),
+                                                    L.ptr(accept_len), L.ptr(next_blocks), L.ptr(logits)))
+
     def commit_kv(self, seq: int, n_accept: int):
         L.check(self.lib.sdm_commit_kv(self.handle, seq, int(n_accept)))
 
