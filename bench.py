@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak
 METRIC = "decoded tokens/s at 1 GPU, 8B-shape self-spec block 32; forward % of HBM roofline"
 
 
@@ -97,6 +98,9 @@ def main() -> int:
     ap.add_argument("--batch14b", action="store_true",
                     help="also measure the 14B-shaped 16-sequence batched diffusion block (draws ~30 GB of weights)")
     ap.add_argument("--no-w4", action="store_true", help="skip the 4-bit weight (w4a16) pass of the extras")
+    ap.add_argument("--no-quadratic", action="store_true", help="skip the quadratic self-speculation pass")
+    ap.add_argument("--quadratic-only", action="store_true",
+                    help="only the quadratic self-speculation pass (for profilers)")
     ap.add_argument("--w4-only", action="store_true", help="only the 4-bit weight (w4a16) pass (for profilers)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
@@ -133,6 +137,10 @@ def main() -> int:
     log(f"weights drawn in {time.time() - t0:.1f}s")
     prompt = W.prompt_ids(s, args.prompt, seed=0)
     sched = W.forced_accept_schedule(8192, B, seed=0)
+    if args.quadratic_only:
+        print(json.dumps({"quadratic": quadratic_bench(log, s, weights, prompt, sched, args.warmup, 4096,
+                                                       n_cyc=args.steps or 40)}), flush=True)
+        return 0
     K = args.steps
     if K is None:
         tot, K = 1, 0
@@ -384,11 +392,17 @@ def main() -> int:
                                             "tpf": round(tokens / (2 * K), 3)},
                         "prefill_1024_ms": round(t_pf * 1e3, 2)}
 
-    if not args.no_extras and not args.no_w4:
+    if not args.no_extras and not args.no_quadratic:
         model.close()
-        del model
-        torch.cuda.empty_cache()
         model = None
+        torch.cuda.empty_cache()
+        out["quadratic"] = quadratic_bench(log, s, weights, prompt, sched, args.warmup, max_ctx,
+                                           linear_tpf=tokens / (2 * K))
+    if not args.no_extras and not args.no_w4:
+        if model is not None:
+            model.close()
+            model = None
+        torch.cuda.empty_cache()
         out["w4a16"] = w4a16_bench(log, s, prompt, sched, K, args.warmup, max_ctx)
 
     if args.calib_copy:
@@ -498,6 +512,114 @@ def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx) -> dict:
             "roofline_gate_up": {"bound": "hbm", "kernel": "k_gemm_w4<EPI_SWIGLU>, M=32", "achieved": round(ach, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                                  "bytes_per_launch": gu["bytes"], "avg_launch_us": gu["avg_us"]}}
+
+
+def gemm_flops(s, cls: str, M: int) -> int:
+    """Flops of one GEMM launch of a class at M rows (2 per multiply-add)."""
+    d, F = s.d_model, s.ffn_dim
+    nk = {"qkv": (s.qkv_dim, d), "o": (d, s.q_dim), "gate_up": (2 * F, d), "down": (d, F), "lm_head": (s.vocab, d)}
+    n, k = nk[cls]
+    return 2 * M * n * k
+
+
+def quadratic_bench(log, s, weights, prompt, sched, warmup, max_ctx, n_cyc=40, linear_tpf=None) -> dict:
+    """Quadratic self-speculation on the headline's 8B shape: after one draft
+    forward, every cycle is a single forward of B + B^2 = 1056 rows (the
+    causal verify and a candidate next block per accept length) and a commit.
+    The headline's forced accept schedule (U{1..32}, seed 0) over n_cyc
+    cycles: tokens/s and tokens per forward; per-class kernel times from HIP
+    events; the gate/up GEMM and the whole forward against the dense bf16
+    MFMA peak (the work is compute-bound: ~16 TFLOP per forward)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from self_speculative_amd.decode import QuadSpecRun, prefill
+    from self_speculative_amd.model import Model
+    B = 32
+    M = B * (B + 1)
+    model = Model(s, weights, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=M)
+    torch.cuda.synchronize()
+    first = prefill(model, 1, prompt)
+    run = QuadSpecRun(model, B, 1, max(1, warmup))
+    run.draft_first(first.data_ptr())
+    wsched = W.forced_accept_schedule(max(1, warmup), B, seed=1)
+    for c in range(warmup):
+        run.cycle(c, int(wsched[c]))
+    torch.cuda.synchronize()
+    model.seq_reset(1)
+    # timed: the first draft forward and n_cyc quadratic cycles on sequence 0
+    first = prefill(model, 0, prompt)
+    run = QuadSpecRun(model, B, 0, n_cyc)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run.draft_first(first.data_ptr())
+    Ls = [run.cycle(c, int(sched[c])) for c in range(n_cyc)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tokens = int(sum(Ls))
+    log(f"quadratic forced: {n_cyc} cycles, {tokens} tokens in {wall * 1e3:.1f} ms -> {tokens / wall:.1f} tok/s")
+    # per-class kernel times (HIP events on the model's stream), sequence 1
+    first = prefill(model, 1, prompt)
+    classes = ["gate_up", "down", "qkv", "o", "attn", "attn_combine", "norm", "lm_head", "finish", "forward"]
+    per_cls = 2
+    ex = W.forced_accept_schedule(per_cls * len(classes), B, seed=2)
+    run = QuadSpecRun(model, B, 1, per_cls * len(classes))
+    run.draft_first(first.data_ptr())
+    per, ns, pos = {}, [], 0
+    for cls in classes:
+        torch.cuda.synchronize()
+        model.timing_start(cls, 4096)
+        for _ in range(per_cls):
+            ns.append(model.seq_length(1))
+            run.cycle(pos, int(ex[pos]))
+            pos += 1
+        n, tot_ms, mn, mx = model.timing_stop()
+        per[cls] = {"launches": n, "avg_us": round(tot_ms / max(1, n) * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                    "max_us": round(mx * 1e3, 2)}
+        if cls in ("gate_up", "down", "qkv", "o", "lm_head"):
+            f = gemm_flops(s, cls, M)
+            per[cls]["flops"] = f
+            per[cls]["TFLOPs"] = round(f / (per[cls]["avg_us"] * 1e-6) / 1e12, 1)
+        log(f"quadratic {cls:>12}: {n} launches, avg {per[cls]['avg_us']} us")
+    # natural accept lengths (random weights: short accepts), 8 cycles
+    model.seq_reset(1)
+    first = prefill(model, 1, prompt)
+    run = QuadSpecRun(model, B, 1, 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run.draft_first(first.data_ptr())
+    Ln = [run.cycle(c, None) for c in range(8)]
+    torch.cuda.synchronize()
+    t_nat = time.perf_counter() - t0
+    model.close()
+    # one forward's work at the mean committed length of the timed classes
+    n = float(np.mean(ns))
+    params = sum(layer_weight_bytes(s).values()) // 2 * s.n_layers + s.vocab * s.d_model
+    keys = B * n + B * (B + 1) / 2 + B * B * n + B * B * (B + 1) / 2 + B ** 3   # (row, visible key) pairs
+    attn_flops = 4 * keys * s.n_q_heads * s.head_dim * s.n_layers
+    fwd_flops = 2 * M * params + attn_flops
+    f_us = per["forward"]["avg_us"]
+    gu = per["gate_up"]
+    ach = gu["flops"] / (gu["avg_us"] * 1e-6) / 1e12
+    return {"workload": "8B shape, prompt 1024, block 32: one draft forward, then per cycle one forward of "
+                        "B + B^2 = 1056 rows (causal verify + a candidate next block per accept length); "
+                        "forced accept U{1..32} seed 0 (the headline schedule)",
+            "cycles": n_cyc, "tokens": tokens, "tok_per_s": round(tokens / wall, 1),
+            "ms_per_cycle": round(wall * 1e3 / n_cyc, 3),
+            "tpf": round(tokens / (n_cyc + 1), 3), "linear_tpf": None if linear_tpf is None else round(linear_tpf, 3),
+            "natural": {"cycles": 8, "tokens": int(sum(Ln)), "mean_accept": round(float(np.mean(Ln)), 3),
+                        "tok_per_s": round(sum(Ln) / t_nat, 1)},
+            "kernels": per,
+            "forward": {"avg_us": f_us, "rows": M, "flops": int(fwd_flops),
+                        "mfma_frac": round(fwd_flops / (f_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+                        "mean_committed_len": round(n, 1)},
+            "roofline_gate_up": {"bound": "mfma", "kernel": f"k_gemm_bf16<EPI_SWIGLU> (gate/up + SwiGLU), M={M}",
+                                 "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": gu["flops"],
+                                 "avg_launch_us": gu["avg_us"],
+                                 "note": "algorithmic flops; the two-term bf16 activations issue two MFMA products "
+                                         "per weight tile, so the matrix units do twice this work"}}
 
 
 def _pct(vals):

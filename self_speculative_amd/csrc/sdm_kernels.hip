@@ -420,6 +420,15 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
 // independent of the batch it is computed in.  With TP > 1, wave t reduces and
 // finishes tile t.
 // ---------------------------------------------------------------------------
+// Weight loads: streamed past the caches when a launch reads each weight tile
+// once (up to 128 activation rows); cached otherwise, so that the activation
+// groups after the first read the matrix from the memory-side cache.
+template <int MT>
+__device__ __forceinline__ u32x4 load_weight(const u32x4* p) {
+  if constexpr (MT < 4) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 template <int EPI, int MT, int TP, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, int64_t x_plane,
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
 #pragma unroll
     for (int t = 0; t < TP; ++t)
 #pragma unroll
-      for (int u = 0; u < U; ++u) wv[t][u] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb + boff(u)) * 64);
+      for (int u = 0; u < U; ++u) wv[t][u] = load_weight<MT>(wp + ((int64_t)t * g.KB + kb + boff(u)) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
@@ -490,7 +499,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   auto one_block = [&](int kb) {
     u32x4 wv[TP];
 #pragma unroll
-    for (int t = 0; t < TP; ++t) wv[t] = __builtin_nontemporal_load(wp + ((int64_t)t * g.KB + kb) * 64);
+    for (int t = 0; t < TP; ++t) wv[t] = load_weight<MT>(wp + ((int64_t)t * g.KB + kb) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
       const int64_t tg = (int64_t)(nt0 + t) * G + gr;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        cw[t][p] = __builtin_nontemporal_load(wc + (tg * 2 + p) * 64);
+        cw[t][p] = load_weight<MT>(wc + (tg * 2 + p) * 64);
         sw[t][p] = ws[tg * 4 + p];
       }
     }
