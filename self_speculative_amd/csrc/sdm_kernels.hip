@@ -301,8 +301,8 @@ __device__ __forceinline__ void epi_preload(EpiPre& p, int nt, int mt, int lane,
 }
 
 template <int EPI, bool PRE>
-__device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int mt, int lane, const EpiArgs& ea,
-                                              const EpiPre& pre_in) {
+__device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int mt, int sk, int lane,
+                                              const EpiArgs& ea, const EpiPre& pre_in) {
   const int h = lane >> 5;
   const int m = mt * 32 + (lane & 31);
   const bool valid = m < ea.M;
@@ -375,7 +375,7 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
   } else if constexpr (EPI == EPI_PARTIAL) {
     if (!valid) return;
     // rows crow(4j + i, h) = 8j + 4h + i: four contiguous floats per j
-    float* pr = ea.part + (int64_t)blockIdx.y * ea.part_stride + (int64_t)m * ea.d + nt * 32 + 4 * h;
+    float* pr = ea.part + (int64_t)sk * ea.part_stride + (int64_t)m * ea.d + nt * 32 + 4 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) *(float4*)(pr + 8 * j) = make_float4(c[4 * j], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]);
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -429,12 +429,45 @@ __device__ __forceinline__ u32x4 load_weight(const u32x4* p) {
   else return *p;
 }
 
+// Workgroup placement of a many-row launch (one-dimensional grid).  Work
+// units are (weight tile group, K split) pairs; activation groups go in bands
+// of eight.  Inside a band of g groups, g dividing 8, workgroup L takes group
+// L % g and unit L / g: workgroups go to the eight XCDs round robin, so each
+// XCD keeps one activation group (L2-resident), and the groups reading one
+// weight tile run at the same time (the tile comes from HBM once).  A band
+// whose group count does not divide 8 runs group by group.
+__device__ __forceinline__ void many_row_place(int L, int units, int groups, int& unit, int& mg) {
+  const int band = L / (units * 8);
+  const int r = L - band * units * 8;
+  const int gb = min(8, groups - 8 * band);
+  if (8 % gb == 0) {
+    mg = 8 * band + r % gb;
+    unit = r / gb;
+  } else {
+    mg = 8 * band + r / units;
+    unit = r % units;
+  }
+}
+
 template <int EPI, int MT, int TP, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, int64_t x_plane,
                                                           GemmShape g, EpiArgs ea) {
   static_assert(TP <= WAVES, "one finishing wave per weight tile");
-  const int nt0 = blockIdx.x * TP, sk = blockIdx.y, mg = blockIdx.z;
+  // grid (weight tile groups, K splits, activation groups); launches of four
+  // activation tiles run a one-dimensional grid placed by many_row_place
+  int nt0, sk, mg;
+  if constexpr (MT == 4) {
+    const int ntg = g.NT / TP;
+    int unit;
+    many_row_place(blockIdx.x, ntg * g.S, (g.MTILES + 3) / 4, unit, mg);
+    nt0 = (unit / g.S) * TP;
+    sk = unit % g.S;
+  } else {
+    nt0 = blockIdx.x * TP;
+    sk = blockIdx.y;
+    mg = blockIdx.z;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int mt0 = mg * MT;
   const int mcount = min(MT, g.MTILES - mt0);
@@ -535,7 +568,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
         for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
         c[r] = v;
       }
-      gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
+      gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, sk, lane, ea, pre);
     }
   } else {
     // the MT x TP output tiles (activation tile major) go through LDS
@@ -564,7 +597,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
           for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
           c[r] = v;
         }
-        gemm_epilogue<EPI, false>(c, nt0 + q % TP, mt0 + q / TP, lane, ea, pre);
+        gemm_epilogue<EPI, false>(c, nt0 + q % TP, mt0 + q / TP, sk, lane, ea, pre);
       }
     }
   }
@@ -575,7 +608,8 @@ static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane,
                           hipStream_t st) {
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
   const int TP = g.TP;
-  const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(64 * WAVES);
+  const int mgroups = (g.MTILES + MT - 1) / MT;
+  const dim3 grd = MT == 4 ? dim3(mgroups * (g.NT / TP) * g.S) : dim3(g.NT / TP, g.S, mgroups), blk(64 * WAVES);
   // weight loads in flight per wave: 16 tiles at TP 1, 4 * TP otherwise
   constexpr int U1 = WAVES == 8 ? 8 : 16;
   if (MT == 1) {
@@ -794,8 +828,8 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
       for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
       c[r] = v;
     }
-    if constexpr (MT == 1) gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, lane, ea, pre);
-    else gemm_epilogue<EPI, false>(c, nt0 + wave % TP, mt0 + wave / TP, lane, ea, pre);
+    if constexpr (MT == 1) gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, sk, lane, ea, pre);
+    else gemm_epilogue<EPI, false>(c, nt0 + wave % TP, mt0 + wave / TP, sk, lane, ea, pre);
   }
 }
 
