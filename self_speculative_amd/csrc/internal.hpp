@@ -13,6 +13,7 @@ constexpr int kAttnSplitKeys = 256;    // keys per attention split (absolute ran
 constexpr int kMaxSlots = 64;          // sequences in one forward
 constexpr int kHd = 128;               // bf16 path head dim
 constexpr int kAttnStagedPairs = 256;  // (split, KV head) pairs from which attention stages splits in LDS
+constexpr int kAttnStreamPairs = 512;  // from which it streams runs of splits (no candidate slots, G*T <= 128)
 
 enum Mode { CAUSAL = 0, BIDIR = 1 };
 enum Epi { EPI_QKV = 0, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };

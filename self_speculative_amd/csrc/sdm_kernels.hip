@@ -1193,6 +1193,115 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
   }
 }
 
+// Long contexts: one workgroup per (slot, KV head, run of ns consecutive
+// splits).  The run's pages stream through two LDS page buffers: all 256
+// threads load page p + 1 into registers while the waves compute page p
+// from the other buffer, then store it and meet at a barrier.  Wave w runs
+// query tile w (four tiles at most) and reads the MFMA operands straight
+// from LDS.  Each split's four page states merge in page order and its
+// partial is written exactly as by the other two shapes, so the results are
+// the same bits.  Not used for candidate slots.
+constexpr int kStreamMaxRun = 64;  // splits per workgroup of the streaming shape
+
+template <bool QLO, bool QPACK>
+__global__ __launch_bounds__(256) void k_attn_stream_bf16(AttnArgs a, int ns) {
+  __shared__ u32x4 s_k[2][16][64];  // a page's K operand tiles, two buffers
+  __shared__ u32x4 s_v[2][16][64];  //            V^T operand tiles
+  __shared__ int s_page[4 * kStreamMaxRun];  // the run's page indices, read once
+  const int slot = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  const int seq = a.slots.ids[slot];
+  const int T = a.slots.T;
+  const int n = a.slots.len[slot];
+  const int nkeys = n + T;
+  const int Hkv = a.kv.Hkv;
+  const int G = a.Hq / Hkv;
+  const int nq = G * T;
+  const int nqt = (nq + 31) >> 5;
+  const int nsp = attn_splits(a.slots, slot);
+  const int g = blockIdx.x % Hkv;
+  const int sp0 = (blockIdx.x / Hkv) * ns;
+  if (sp0 >= nsp) return;
+  const int npages = (min(nsp, sp0 + ns) - sp0) * 4;
+  const int key0 = sp0 * kAttnSplitKeys;
+  for (int p = tid; p < npages; p += 256) {
+    const int jw = key0 + 64 * p;
+    s_page[p] = jw < nkeys ? a.kv.page_table[(int64_t)seq * a.kv.max_pages + jw / kPageTokens] : 0;
+  }
+  __syncthreads();
+  // page p of the run: K block then V block of head g, 1024 vectors each;
+  // thread tid moves vectors tid + 256 r of both
+  u32x4 rk[4], rv[4];
+  auto load_page = [&](int p) {
+    const int jw = key0 + 64 * p;
+    if (jw < nkeys) {
+      const uint16_t* pb = (const uint16_t*)a.kv.pool + (int64_t)s_page[p] * a.kv.page_elems + a.kv.layer_off;
+      const u32x4* kb = (const u32x4*)(pb + (int64_t)g * kPageTokens * kHd);
+      const u32x4* vb = (const u32x4*)(pb + (int64_t)(Hkv + g) * kPageTokens * kHd);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rk[r] = kb[tid + 256 * r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rv[r] = vb[tid + 256 * r];
+    }
+  };
+  auto store_page = [&](int p, int buf) {
+    if (key0 + 64 * p < nkeys) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) (&s_k[buf][0][0])[tid + 256 * r] = rk[r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) (&s_v[buf][0][0])[tid + 256 * r] = rv[r];
+    }
+  };
+  const int qt = wave;
+  const bool tile = qt < nqt;
+  const int c = qt * 32 + (lane & 31);
+  const bool cval = tile && c < nq;
+  const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
+  u32x4 qop[8], qlo[QLO ? 8 : 1];
+  if (tile) attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
+  load_page(0);
+  store_page(0, 0);
+  __syncthreads();
+  AttnState run, pg;
+  for (int sp = 0; 4 * sp < npages; ++sp) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // page w of the split, in LDS buffer w & 1
+      const int p = 4 * sp + w;
+      if (p + 1 < npages) load_page(p + 1);
+      if (tile) {
+        AttnState& st = w == 0 ? run : pg;
+        attn_page_state<QLO>(a, [&](int i) { return s_k[w & 1][i][lane]; },
+                             [&](int i) { return s_v[w & 1][i][lane]; }, qop, qlo, key0 + 64 * p, nkeys, n, n + t,
+                             cval, h, st);
+        if (w > 0) {
+          float M, ca, cb;
+          attn_merge_coef(run.m, pg.m, M, ca, cb);
+          run.l = ca * run.l + cb * pg.l;
+          run.m = M;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) run.o[dt][r] = ca * run.o[dt][r] + cb * pg.o[dt][r];
+        }
+        if (w == 3 && cval) {
+          const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp0 + sp;
+          float* op = a.opart + base_idx * kHd * a.nq_pad + c;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) op[(int64_t)(dt * 32 + crow(r, h)) * a.nq_pad] = run.o[dt][r];
+          if (h == 0) {
+            a.mlpart[(base_idx * 2 + 0) * a.nq_pad + c] = run.m;
+            a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = run.l;
+          }
+        }
+      }
+      if (p + 1 < npages) store_page(p + 1, (w & 1) ^ 1);
+      __syncthreads();
+    }
+  }
+}
+
 // Merge the splits for 32 query columns x 16 dims of one (slot, KV head):
 // o = sum_s w_s O_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s), split
 // order fixed; written as bf16 (hi, plus the lo plane when out_plane is set).
@@ -1276,6 +1385,16 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st) {
   const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
   const int pairs = grid_splits * a.kv.Hkv;
+  // long contexts: stream runs of splits through LDS, at least two
+  // workgroups per compute unit
+  if (a.slots.xslot0 == 0 && nqt <= 4 && (int64_t)pairs * a.slots.n_seq >= kAttnStreamPairs) {
+    const int ns = std::min(kStreamMaxRun, std::max(1, (int)((int64_t)pairs * a.slots.n_seq / kAttnStreamPairs)));
+    const dim3 grd(a.kv.Hkv * ((grid_splits + ns - 1) / ns), a.slots.n_seq), blk(256);
+    if (a.q_plane && a.q_packed) SDM_LAUNCH((k_attn_stream_bf16<true, true>), grd, blk, 0, st, a, ns);
+    else if (!a.q_plane && !a.q_packed) SDM_LAUNCH((k_attn_stream_bf16<false, false>), grd, blk, 0, st, a, ns);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   // enough (split, head) pairs to cover the chip: stage each split once and
   // run all its query tiles (same results as the tile-parallel shape)
   const bool staged = (int64_t)pairs * a.slots.n_seq >= kAttnStagedPairs;

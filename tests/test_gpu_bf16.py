@@ -301,6 +301,34 @@ def test_bf16_staged_attention_matches_tile_parallel(weights, om):
     m.close()
 
 
+def test_bf16_streamed_attention_matches_tile_parallel(weights):
+    """A batch with at least 512 (split, KV head) pairs streams runs of splits
+    through LDS; alone, each sequence runs the tile-parallel shape.  Both must
+    give the same bits."""
+    from self_speculative_amd.model import Model
+    lens = [3900 + 37 * i for i in range(16)]           # 16+ splits x 2 KV heads x 16 = 512+ pairs
+    m = Model(SHAPE, weights, max_seqs=16, max_block=B, max_context=4608, max_rows=16 * B)
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    for i, n in enumerate(lens):
+        m.prefill(i, _i32(W.prompt_ids(SHAPE, n, seed=33, index=i)), nxt)
+    seqs = list(range(16))
+    blk = torch.full((16, B), SHAPE.mask_id, dtype=torch.int32, device=DEV)
+    nm = torch.empty(16, dtype=torch.int32, device=DEV)
+    lg = torch.empty((16 * B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+    print("bf16 streamed attention: batch of 16", flush=True)
+    m.diffuse_step(seqs, blk, B, 0.9, False, nm, None, lg)
+    torch.cuda.synchronize()
+    batch = lg.cpu().numpy()
+    for i in (0, 7, 15):
+        print(f"bf16 streamed attention: sequence {i} alone", flush=True)
+        b1 = torch.full((1, B), SHAPE.mask_id, dtype=torch.int32, device=DEV)
+        l1 = torch.empty((B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+        m.diffuse_step([i], b1, B, 0.9, False, nm[:1], None, l1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(l1.cpu().numpy(), batch[i * B:(i + 1) * B])
+    m.close()
+
+
 def test_bf16_shuffled_pages_bit_identical(weights):
     from self_speculative_amd.model import Model
     from self_speculative_amd import decode as D
