@@ -163,7 +163,7 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
     // tiles per group
     auto ok = [&](int s) { return s <= kMaxSplitK && g.KB % s == 0 && g.KB / s >= 32; };
     while (g.NT * g.S < 2 * kGemmTargetGroups && ok(2 * g.S)) g.S *= 2;
-    while (ok(2 * g.S) && g.KB / (2 * g.S) >= 96 && g.NT * 2 * g.S <= 4 * kGemmTargetGroups) g.S *= 2;
+    while (ok(2 * g.S) && g.KB / (2 * g.S) >= 192 && g.NT * 2 * g.S <= 4 * kGemmTargetGroups) g.S *= 2;
   }
   g.WAVES = 4;
   g.TP = 1;

@@ -878,13 +878,17 @@ hipError_t launch_gemm_w4(int epi, const uint8_t* W, const uint16_t* X, int64_t 
 // split's partial; the combine kernel merges splits in split order.  Masked
 // keys contribute exact zeros and every key range is absolute, so a row's
 // result does not depend on how many rows the block has -- nor on which of
-// the two launch shapes below computed it:
+// the three launch shapes below computed it:
 //   k_attn_bf16        one workgroup per (split, KV head, query tile); wave w
 //                      takes page w into registers, the page states meet in
 //                      LDS (short contexts: many small workgroups);
 //   k_attn_staged_bf16 one workgroup per (split, KV head); the four pages go
 //                      through LDS once and wave t runs query tile t over all
-//                      four (long contexts and batches).
+//                      four (long contexts and batches);
+//   k_attn_stream_bf16 one workgroup per run of splits of a KV head; pages
+//                      stream through two LDS buffers, the next one loading
+//                      while the current one is computed (long contexts with
+//                      at most four query tiles, no candidate slots).
 // ---------------------------------------------------------------------------
 struct AttnState {
   float m, l;
