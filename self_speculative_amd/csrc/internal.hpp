@@ -159,8 +159,9 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   if (epi == EPI_PARTIAL) {
     // enough splits for two workgroups per compute unit (two waves per SIMD,
     // so one-tile groups overlap their accumulator chains); more while every
-    // split still streams at least 96 k-blocks (long-K matrices), up to four
-    // tiles per group
+    // split would still stream at least 192 k-blocks (very long K), up to
+    // four tiles per group.  Fewer splits mean fewer partial planes for the
+    // following RMSNorm to add (and to write and read at many rows).
     auto ok = [&](int s) { return s <= kMaxSplitK && g.KB % s == 0 && g.KB / s >= 32; };
     while (g.NT * g.S < 2 * kGemmTargetGroups && ok(2 * g.S)) g.S *= 2;
     while (ok(2 * g.S) && g.KB / (2 * g.S) >= 192 && g.NT * 2 * g.S <= 4 * kGemmTargetGroups) g.S *= 2;
