@@ -21,6 +21,7 @@
 #include <cstdint>
 
 #include "internal.hpp"
+#include "placement.hpp"
 
 namespace sdm {
 
@@ -429,26 +430,6 @@ __device__ __forceinline__ u32x4 load_weight(const u32x4* p) {
   else return *p;
 }
 
-// Workgroup placement of a many-row launch (one-dimensional grid).  Work
-// units are (weight tile group, K split) pairs; activation groups go in bands
-// of eight.  Inside a band of g groups, g dividing 8, workgroup L takes group
-// L % g and unit L / g: workgroups go to the eight XCDs round robin, so each
-// XCD keeps one activation group (L2-resident), and the groups reading one
-// weight tile run at the same time (the tile comes from HBM once).  A band
-// whose group count does not divide 8 runs group by group.
-__device__ __forceinline__ void many_row_place(int L, int units, int groups, int& unit, int& mg) {
-  const int band = L / (units * 8);
-  const int r = L - band * units * 8;
-  const int gb = min(8, groups - 8 * band);
-  if (8 % gb == 0) {
-    mg = 8 * band + r % gb;
-    unit = r / gb;
-  } else {
-    mg = 8 * band + r / units;
-    unit = r % units;
-  }
-}
-
 template <int EPI, int MT, int TP, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, int64_t x_plane,
@@ -459,10 +440,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   int nt0, sk, mg;
   if constexpr (MT == 4) {
     const int ntg = g.NT / TP;
-    int unit;
-    many_row_place(blockIdx.x, ntg * g.S, (g.MTILES + 3) / 4, unit, mg);
-    nt0 = (unit / g.S) * TP;
-    sk = unit % g.S;
+    const ManyRowPlace pl = many_row_place(blockIdx.x, ntg * g.S, (g.MTILES + 3) / 4);
+    mg = pl.group;
+    nt0 = (pl.unit / g.S) * TP;
+    sk = pl.unit % g.S;
   } else {
     nt0 = blockIdx.x * TP;
     sk = blockIdx.y;

@@ -1,5 +1,6 @@
-"""Host-only C++ unit tests (no GPU): the KV page allocator, built with g++
-and the address / undefined-behaviour sanitizers, then run."""
+"""Host-only C++ unit tests (no GPU), built with g++ and the address /
+undefined-behaviour sanitizers, then run: the KV page allocator and the
+workgroup placement of the many-row GEMM launches."""
 import os
 import shutil
 import subprocess
@@ -18,6 +19,20 @@ def test_page_pool_sanitized(tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     # the sanitizer runtime need not come first among preloaded libraries
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_many_row_placement_sanitized(tmp_path):
+    exe = str(tmp_path / "test_placement")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-I", os.path.join(ROOT, "self_speculative_amd", "csrc"),
+           os.path.join(ROOT, "tests", "cpp", "test_placement.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
     r = subprocess.run([exe], capture_output=True, text=True, env=env)
     assert r.returncode == 0, r.stdout + r.stderr
