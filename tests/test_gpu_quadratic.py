@@ -97,6 +97,29 @@ def test_tiny_quadratic_streams(tiny_gm, tiny_om, B):
     assert gf.tokens == of.tokens and gf.accept_lengths == of.accept_lengths
 
 
+def test_tiny_quadratic_extreme_blocks(tiny_om):
+    """The smallest block (B = 2) and the largest (B = 63: 64 slots, 4032-row
+    forwards): streams equal the oracle's, natural and forced."""
+    from self_speculative_amd import decode as D
+    from self_speculative_amd.model import Model
+    m = Model(TINY, W.make_weights(TINY, seed=0), max_seqs=2, max_block=63, max_context=512, max_rows=63 * 64)
+    try:
+        p = W.prompt_ids(TINY, 16, seed=0)
+        for B, n, forced in ((2, 24, [2, 1, 2, 2, 1, 2]), (63, 6, [63, 1, 40])):
+            print(f"tiny quadratic B={B}", flush=True)
+            m.seq_reset(0)
+            g = D.generate_selfspec_quadratic(m, p, n, B, seq=0)
+            o = O.generate_selfspec_quadratic(tiny_om, p, n, B)
+            assert g.tokens == o.tokens and g.accept_lengths == o.accept_lengths, B
+            m.seq_reset(1)
+            nf = 1 + sum(forced)
+            gf = D.generate_selfspec_quadratic(m, p, nf, B, forced=forced, seq=1)
+            of = O.generate_selfspec_quadratic(tiny_om, p, nf, B, forced=forced)
+            assert gf.tokens == of.tokens, B
+    finally:
+        m.close()
+
+
 def test_tiny_quadratic_lockstep_rows(tiny_gm, tiny_om):
     B = 8
     seq = 2
@@ -161,6 +184,33 @@ def test_bf16_quadratic_lockstep(small_gm, small_w):
     print(f"bf16 quadratic: max|dlogit| {rep.max_logit_err:.3e}, tokens {rep.compared_tokens}, "
           f"exempt {rep.exempt}, resyncs {rep.resyncs}", flush=True)
     assert rep.max_logit_err <= 2e-2
+
+
+def test_bf16_quadratic_largest_block_lockstep(small_w):
+    """B = 63: 64 slots and 4032-row forwards (32 activation groups of the
+    many-row GEMMs, four placement bands) in lockstep with the oracle."""
+    from self_speculative_amd.model import Model
+    B = 63
+    m = Model(SMALL, small_w, max_seqs=1, max_block=B, max_context=512, max_rows=B * (B + 1))
+    try:
+        sess = O.OracleSession(O.OracleModel(SMALL, small_w))
+        p = W.prompt_ids(SMALL, 70, seed=26)
+        nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+        m.prefill(0, _i32(p), nxt)
+        g = int(sess.prefill(0, p).tok[0])
+        blk = torch.empty(B, dtype=torch.int32, device=DEV)
+        m.draft_block(0, _i32([g]), B, blk)
+        oblk, _ = sess.draft_block(0, g, B)
+        rep = Report()
+        lg = torch.empty((B * (B + 1), SMALL.vocab), dtype=torch.float32, device=DEV)
+        for cyc, L in enumerate([None, 63]):
+            print(f"bf16 quadratic B=63 cycle {cyc}", flush=True)
+            oblk, _ = _quad_lockstep(m, sess, 0, oblk, B, rep, lg, L)
+        print(f"bf16 quadratic B=63: max|dlogit| {rep.max_logit_err:.3e}, tokens {rep.compared_tokens}, "
+              f"exempt {rep.exempt}", flush=True)
+        assert rep.max_logit_err <= 2e-2
+    finally:
+        m.close()
 
 
 def test_bf16_quadratic_equals_ar_on_gpu(small_gm):
