@@ -149,7 +149,7 @@ def main() -> int:
             K += 1
     max_ctx = 4096 if args.prompt + args.gen_tokens + 2 * B <= 4096 else args.prompt + args.gen_tokens + 1024
     t0 = time.time()
-    model = Model(s, weights, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=128)
+    model = Model(s, weights, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=1024)
     torch.cuda.synchronize()
     log(f"model uploaded + packed in {time.time() - t0:.1f}s ({model.weight_bytes / 1e9:.2f} GB)")
     dev = model.device
@@ -440,7 +440,7 @@ def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx) -> dict:
     t0 = time.time()
     w = W.make_w4_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
     log(f"w4a16: weights drawn in {time.time() - t0:.1f}s")
-    model = Model(s, w, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=128, free_host=True)
+    model = Model(s, w, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=1024, free_host=True)
     del w
     torch.cuda.synchronize()
     log(f"w4a16: model uploaded + packed ({model.weight_bytes / 1e9:.2f} GB)")

@@ -1,8 +1,8 @@
 """GPU parity at the full model shapes.
 
 * 8B (36 layers, d 4096, 32/8 heads, FFN 12288, vocab 151936) in exactly the
-  launch configuration bench.py times (prompt 1024, 32-row blocks, 128-row
-  prefill chunks): prefill, a draft, a verify, a commit and an AR step in
+  launch configuration bench.py times (prompt 1024 in one 1024-row prefill
+  chunk, 32-row blocks): prefill, a draft, a verify, a commit and an AR step in
   lockstep with the float64 oracle -- every logit of every row compared.
 * 3B (28 layers): self-speculation and block diffusion windows in lockstep.
 * 14B width: oracle lockstep on the shape truncated to 2 layers (the per-layer
@@ -101,7 +101,7 @@ def test_8b_bench_configuration_lockstep():
     print("8b: drawing weights", flush=True)
     w = W.make_weights(s, seed=0)
     prompt = W.prompt_ids(s, 1024, seed=0)
-    gm = Model(s, w, max_seqs=2, max_block=B, max_context=4096, max_rows=128)
+    gm = Model(s, w, max_seqs=2, max_block=B, max_context=4096, max_rows=1024)
     om = O.OracleModel(s, w)
     sess = O.OracleSession(om)
     rep = Report()
