@@ -201,7 +201,7 @@ def test_w4_8b_bench_configuration_lockstep():
     print("w4 8b: drawing weights", flush=True)
     w = W.make_w4_weights(s, seed=0)
     prompt = W.prompt_ids(s, 1024, seed=0)
-    gm = Model(s, w, max_seqs=1, max_block=B, max_context=2048, max_rows=1024)
+    gm = Model(s, w, max_seqs=1, max_block=B, max_context=2048, max_rows=128)
     om = O.OracleModel(s, w)
     sess = O.OracleSession(om)
     rep = Report()
