@@ -106,8 +106,8 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not part of it "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py: runs on exactly one GPU; multi-GPU runs are not supported (the path's sharding across "
+              "GPUs is a design, not an implementation)", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -57,7 +57,7 @@ typedef enum {
   SDM_ERR_STATE = -2,      /* call not allowed in the sequence's state        */
   SDM_ERR_CAPACITY = -3,   /* KV pool / context / workspace / seq slots full  */
   SDM_ERR_DEVICE = -4,     /* a HIP call failed; sticky for the handle        */
-  SDM_ERR_UNSUPPORTED = -5 /* shape or dtype this build does not implement    */
+  SDM_ERR_UNSUPPORTED = -5 /* shape or dtype the library does not implement  */
 } sdm_status;
 
 typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
