@@ -12,7 +12,7 @@ constexpr int kPageTokens = 64;        // KV page size (positions per page)
 constexpr int kAttnSplitKeys = 256;    // keys per attention split (absolute ranges)
 constexpr int kMaxSlots = 64;          // sequences in one forward
 constexpr int kHd = 128;               // bf16 path head dim
-constexpr int kAttnStagedPairs = 256;  // (split, KV head) pairs from which attention stages splits in LDS
+constexpr int kAttnStagedPairs = 256;  // (split, KV head, query-tile group) units from which splits are staged in LDS
 constexpr int kAttnStreamPairs = 512;  // from which it streams runs of splits (no candidate slots, G*T <= 128)
 
 enum Mode { CAUSAL = 0, BIDIR = 1 };

@@ -863,9 +863,11 @@ hipError_t launch_gemm_w4(int epi, const uint8_t* W, const uint16_t* X, int64_t 
 //   k_attn_bf16        one workgroup per (split, KV head, query tile); wave w
 //                      takes page w into registers, the page states meet in
 //                      LDS (short contexts: many small workgroups);
-//   k_attn_staged_bf16 one workgroup per (split, KV head); the four pages go
-//                      through LDS once and wave t runs query tile t over all
-//                      four (long contexts and batches);
+//   k_attn_staged_bf16 one workgroup per (split, KV head, group of query
+//                      tiles: four, the last up to seven); the four pages go
+//                      through LDS once and wave t runs the group's query
+//                      tiles t, t+4 over all four (long contexts, batches and
+//                      many-row prefill chunks);
 //   k_attn_stream_bf16 one workgroup per run of splits of a KV head; pages
 //                      stream through two LDS buffers, the next one loading
 //                      while the current one is computed (long contexts with
@@ -1110,7 +1112,13 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
   const int nq = G * T;
   const int nqt = (nq + 31) >> 5;
   const int nsp = attn_splits(a.slots, slot);
-  const int pair = blockIdx.x;
+  // linear id -> (pair = split * Hkv + g, group of query tiles); the groups
+  // of a pair get ids congruent mod 8, so they share an XCD's L2.  Groups
+  // hold four tiles; the last one also takes the remainder (up to seven)
+  const int nqg = nqt >= 8 ? nqt >> 2 : 1;
+  const int L = blockIdx.x;
+  const int qg = (L % (8 * nqg)) / 8;
+  const int pair = (L / (8 * nqg)) * 8 + (L % 8);
   if (pair >= nsp * Hkv) return;
   const int sp = pair / Hkv, g = pair % Hkv;
   const AttnKeys ks = attn_keys(a, slot, n, T, sp, nsp);
@@ -1132,7 +1140,8 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
     }
   }
   __syncthreads();
-  for (int qt = wave; qt < nqt; qt += 4) {
+  const int qt_end = qg == nqg - 1 ? nqt : 4 * qg + 4;
+  for (int qt = 4 * qg + wave; qt < qt_end; qt += 4) {
     const int c = qt * 32 + (lane & 31);
     const bool cval = c < nq;
     const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
@@ -1380,10 +1389,13 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  // enough (split, head) pairs to cover the chip: stage each split once and
-  // run all its query tiles (same results as the tile-parallel shape)
-  const bool staged = (int64_t)pairs * a.slots.n_seq >= kAttnStagedPairs;
-  const dim3 grd(staged ? pairs : (pairs + 7) / 8 * 8 * nqt, a.slots.n_seq), blk(256);
+  // enough (split, head, group of four query tiles) triples to cover the
+  // chip: stage each split once per group and run the group's query tiles
+  // (same results as the tile-parallel shape, which reads every page once
+  // per query tile)
+  const int nqg = nqt >= 8 ? nqt / 4 : 1;
+  const bool staged = (int64_t)pairs * nqg * a.slots.n_seq >= kAttnStagedPairs;
+  const dim3 grd(staged ? (pairs + 7) / 8 * 8 * nqg : (pairs + 7) / 8 * 8 * nqt, a.slots.n_seq), blk(256);
   if (a.q_plane && a.q_packed) {
     if (staged) SDM_LAUNCH((k_attn_staged_bf16<true, true>), grd, blk, 0, st, a);
     else SDM_LAUNCH((k_attn_bf16<true, true>), grd, blk, 0, st, a);

@@ -329,6 +329,29 @@ def test_bf16_streamed_attention_matches_tile_parallel(weights):
     m.close()
 
 
+def test_bf16_prefill_chunking_bit_identical(weights):
+    """A 2000-token prompt prefilled in one 2000-row chunk (125 query tiles:
+    attention runs the staged shape in groups of four query tiles) and in
+    128-row chunks (the tile-parallel shape) gives the same last-row logits
+    and next token, and the same AR steps after it."""
+    from self_speculative_amd.model import Model
+    p = W.prompt_ids(SHAPE, 2000, seed=34)
+    outs = []
+    for rows in (2000, 128):
+        print(f"bf16 prefill chunking: {rows}-row chunks", flush=True)
+        m = Model(SHAPE, weights, max_seqs=1, max_block=B, max_context=2048, max_rows=rows)
+        toks = torch.empty(5, dtype=torch.int32, device=DEV)
+        lg = torch.empty((5, SHAPE.vocab), dtype=torch.float32, device=DEV)
+        m.prefill(0, _i32(p), toks[0:1], lg[0:1])
+        for t in range(1, 5):
+            m.decode_ar(0, toks[t - 1:t], toks[t:t + 1], lg[t:t + 1])
+        torch.cuda.synchronize()
+        outs.append((toks.cpu().numpy(), lg.cpu().numpy()))
+        m.close()
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
 def test_bf16_shuffled_pages_bit_identical(weights):
     from self_speculative_amd.model import Model
     from self_speculative_amd import decode as D
