@@ -37,6 +37,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// Two values at once with the hardware packed conversion (v_cvt_pk_bf16_f32):
+// the same round to nearest, ties to even as f2bf; a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 // Second term of the two-term bf16 expansion of x whose first term is hi
 // (x - hi is exact in fp32).
 __device__ __forceinline__ uint16_t f2bf_lo(float x, uint16_t hi) { return f2bf(x - bf2f(hi)); }
@@ -880,7 +887,9 @@ struct AttnState {
 
 // State of one page (keys [jw, jw + 64)) for this lane's query column.
 // kop(i) / vop(i) give the page's K / V^T operand tile i for this lane.
-template <bool QLO, class KOp, class VOp>
+// VFAST: a 32-key tile below both n and nkeys skips the per-key visibility
+// test (same values; off where the extra code would spill registers).
+template <bool QLO, bool VFAST, class KOp, class VOp>
 __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp vop, const u32x4 (&qop)[8],
                                                 const u32x4 (&qlo)[QLO ? 8 : 1], int jw, int nkeys, int n,
                                                 int qpos, bool cval, int h, AttnState& st) {
@@ -902,12 +911,21 @@ __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp 
     }
     float sv[16];
     float mx = -INFINITY;
+    if (VFAST && jt + 32 <= n && jt + 32 <= nkeys) {
+      // every key of the tile exists and is committed: visible to every row
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = jt + crow(r, h);
-      const bool vis = cval && j < nkeys && (j < n || a.mode == BIDIR || j <= qpos);
-      sv[r] = vis ? sacc[r] * a.scale : -INFINITY;
-      mx = fmaxf(mx, sv[r]);
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = cval ? sacc[r] * a.scale : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jt + crow(r, h);
+        const bool vis = cval && j < nkeys && (j < n || a.mode == BIDIR || j <= qpos);
+        sv[r] = vis ? sacc[r] * a.scale : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m, mx);
@@ -927,18 +945,14 @@ __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp 
       for (int r = 0; r < 16; ++r) st.o[i][r] *= alpha;
 #pragma unroll
     for (int ka = 0; ka < 2; ++ka) {
-      uint16_t hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = sv[8 * ka + e];
-        hi[e] = f2bf(p);
-        lo[e] = f2bf(p - bf2f(hi[e]));
-      }
+      // P as two bf16 terms: hi = R(p), lo = R(p - hi), two values at a time
       u32x4 phi, plo;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        phi[e] = (uint32_t)hi[2 * e] | ((uint32_t)hi[2 * e + 1] << 16);
-        plo[e] = (uint32_t)lo[2 * e] | ((uint32_t)lo[2 * e + 1] << 16);
+        const float p0 = sv[8 * ka + 2 * e], p1 = sv[8 * ka + 2 * e + 1];
+        const uint32_t hp = f2bf2(p0, p1);
+        phi[e] = hp;
+        plo[e] = f2bf2(p0 - __uint_as_float(hp << 16), p1 - __uint_as_float(hp & 0xffff0000u));
       }
       const int kbv = 2 * kt + ka;  // 16-key group inside the page
 #pragma unroll
@@ -1059,7 +1073,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   u32x4 qop[8], qlo[QLO ? 8 : 1];
   attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
   AttnState st;
-  attn_page_state<QLO>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, ks.jend,
+  attn_page_state<QLO, true>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, ks.jend,
                        ks.jall, n + t, cval, h, st);
   // the page states meet in LDS; per column, merged in page order
   if (h == 0) {
@@ -1159,7 +1173,7 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
       for (int i = 0; i < 16; ++i) pk[i] = s_k[w][i][lane];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i] = s_v[w][i][lane];
-      attn_page_state<QLO>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, ks.jend,
+      attn_page_state<QLO, false>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, ks.jend,
                            ks.jall, n + t, cval, h, st);
       if (w > 0) {
         float M, ca, cb;
@@ -1264,7 +1278,7 @@ __global__ __launch_bounds__(256) void k_attn_stream_bf16(AttnArgs a, int ns) {
       if (p + 1 < npages) load_page(p + 1);
       if (tile) {
         AttnState& st = w == 0 ? run : pg;
-        attn_page_state<QLO>(a, [&](int i) { return s_k[w & 1][i][lane]; },
+        attn_page_state<QLO, true>(a, [&](int i) { return s_k[w & 1][i][lane]; },
                              [&](int i) { return s_v[w & 1][i][lane]; }, qop, qlo, key0 + 64 * p, nkeys, n, n + t,
                              cval, h, st);
         if (w > 0) {
