@@ -887,9 +887,7 @@ struct AttnState {
 
 // State of one page (keys [jw, jw + 64)) for this lane's query column.
 // kop(i) / vop(i) give the page's K / V^T operand tile i for this lane.
-// VFAST: a 32-key tile below both n and nkeys skips the per-key visibility
-// test (same values; off where the extra code would spill registers).
-template <bool QLO, bool VFAST, class KOp, class VOp>
+template <bool QLO, class KOp, class VOp>
 __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp vop, const u32x4 (&qop)[8],
                                                 const u32x4 (&qlo)[QLO ? 8 : 1], int jw, int nkeys, int n,
                                                 int qpos, bool cval, int h, AttnState& st) {
@@ -898,6 +896,10 @@ __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp 
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.o[i] = f32x16{0};
   const int jw1 = min(jw + 64, nkeys);
+  // key j is visible to this lane's query iff j < nkeys and (j < n, or the
+  // block is bidirectional, or j <= qpos): one bound per lane, 0 (none) for a
+  // column past the query tiles
+  const int lim = !cval ? 0 : a.mode == BIDIR ? nkeys : min(nkeys, max(n, qpos + 1));
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int jt = jw + 32 * kt;
@@ -911,21 +913,13 @@ __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp 
     }
     float sv[16];
     float mx = -INFINITY;
-    if (VFAST && jt + 32 <= n && jt + 32 <= nkeys) {
-      // every key of the tile exists and is committed: visible to every row
+    // key jt + crow(r, h) is visible iff it is below lim: crow(r, h) - 4h is a
+    // compile-time row offset
+    const int lt = lim - jt - 4 * h;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = cval ? sacc[r] * a.scale : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jt + crow(r, h);
-        const bool vis = cval && j < nkeys && (j < n || a.mode == BIDIR || j <= qpos);
-        sv[r] = vis ? sacc[r] * a.scale : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      sv[r] = (8 * (r >> 2) + (r & 3)) < lt ? sacc[r] * a.scale : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m, mx);
@@ -1073,7 +1067,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   u32x4 qop[8], qlo[QLO ? 8 : 1];
   attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
   AttnState st;
-  attn_page_state<QLO, true>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, ks.jend,
+  attn_page_state<QLO>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, ks.jend,
                        ks.jall, n + t, cval, h, st);
   // the page states meet in LDS; per column, merged in page order
   if (h == 0) {
@@ -1173,7 +1167,7 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
       for (int i = 0; i < 16; ++i) pk[i] = s_k[w][i][lane];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i] = s_v[w][i][lane];
-      attn_page_state<QLO, false>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, ks.jend,
+      attn_page_state<QLO>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo, jw, ks.jend,
                            ks.jall, n + t, cval, h, st);
       if (w > 0) {
         float M, ca, cb;
@@ -1278,7 +1272,7 @@ __global__ __launch_bounds__(256) void k_attn_stream_bf16(AttnArgs a, int ns) {
       if (p + 1 < npages) load_page(p + 1);
       if (tile) {
         AttnState& st = w == 0 ? run : pg;
-        attn_page_state<QLO, true>(a, [&](int i) { return s_k[w & 1][i][lane]; },
+        attn_page_state<QLO>(a, [&](int i) { return s_k[w & 1][i][lane]; },
                              [&](int i) { return s_v[w & 1][i][lane]; }, qop, qlo, key0 + 64 * p, nkeys, n, n + t,
                              cval, h, st);
         if (w > 0) {
