@@ -924,10 +924,13 @@ __device__ __forceinline__ void attn_page_state(const AttnArgs& a, KOp kop, VOp 
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m, mx);
     const float alpha = (st.m == -INFINITY) ? 0.f : __expf(st.m - m_new);
+    // a masked score (-inf) gives exp(-inf) = 0; m_safe keeps a lane whose
+    // keys are all masked so far (m_new = -inf) away from -inf - -inf
+    const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sv[r] = (sv[r] == -INFINITY) ? 0.f : __expf(sv[r] - m_new);
+      sv[r] = __expf(sv[r] - m_safe);
       psum += sv[r];
     }
     psum += __shfl_xor(psum, 32);
