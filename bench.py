@@ -4,13 +4,16 @@
 SwiGLU 12288, vocab 151936, bf16), single query, prompt 1024, block 32,
 2048 generated tokens, accept length per cycle drawn from a seeded uniform
 schedule over {1..32} (random weights accept ~1 token naturally, the schedule
-exercises long accepts).  A step is one self-speculation cycle: a
-bidirectional draft forward, a causal verify forward and the KV commit.
+exercises long accepts).  A step is one whole generation: the cycles (a
+bidirectional draft forward, a causal verify forward and the KV commit) that
+take the sequence from its 1024-token prompt to 2048 emitted tokens.  Each
+timed step runs on its own sequence, prefilled before the timed region.
 
 Prints one JSON line (rank 0, N = 1).  Also reported: the roofline of the
 dominant kernel (the gate/up GEMM, measured with HIP events on the model's
 stream), per-kernel and per-forward latencies, AR and natural-accept
-self-speculation rates, and the CPU oracle timed on a bounded sample.
+self-speculation rates, the 3B and 14B-batch workloads, the 4-bit weight and
+quadratic variants, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -87,7 +90,8 @@ def measured_traffic():
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed self-spec cycles (default: 2048 tokens)")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps, each one whole generation of --gen-tokens tokens on its own sequence (default 3)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--gen-tokens", type=int, default=2048)
     ap.add_argument("--prompt", type=int, default=1024)
@@ -95,8 +99,11 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="headline pass only (for profilers)")
     ap.add_argument("--attention-op-only", action="store_true",
                     help="run only the standalone attention op measurement (for profilers) and print it")
-    ap.add_argument("--batch14b", action="store_true",
-                    help="also measure the 14B-shaped 16-sequence batched diffusion block (draws ~30 GB of weights)")
+    ap.add_argument("--no-batch14b", action="store_true",
+                    help="skip the 14B-shaped 16-sequence batched diffusion pass (draws ~30 GB of weights)")
+    ap.add_argument("--batch14b-only", action="store_true", help="only the 14B batched diffusion pass (for profilers)")
+    ap.add_argument("--batch14b-tokens", type=int, default=1024, help="generated tokens per sequence of the 14B pass")
+    ap.add_argument("--no-3b", action="store_true", help="skip the 3B-shaped decoder pass")
     ap.add_argument("--no-w4", action="store_true", help="skip the 4-bit weight (w4a16) pass of the extras")
     ap.add_argument("--no-quadratic", action="store_true", help="skip the quadratic self-speculation pass")
     ap.add_argument("--quadratic-only", action="store_true",
@@ -124,76 +131,94 @@ def main() -> int:
     if args.attention_op_only:
         print(json.dumps({"attention_op": attention_op_bench(log)}), flush=True)
         return 0
+    if args.batch14b_only:
+        print(json.dumps({"batch_14b": batch14b_bench(log, n_gen=args.batch14b_tokens)}), flush=True)
+        return 0
     s = W.SHAPES["8b"]
     B = 32
+    sched = W.forced_accept_schedule(8192, B, seed=0)
+    # one step = one whole generation: y1 comes from the prefill, then forced
+    # cycles until gen_tokens tokens have been emitted (the last cycle's
+    # overshoot is discarded)
+    gen_cyc, tot = 0, 1
+    while tot < args.gen_tokens:
+        tot += int(sched[gen_cyc])
+        gen_cyc += 1
     if args.w4_only:
-        sched = W.forced_accept_schedule(8192, B, seed=0)
-        K = args.steps or 115
-        print(json.dumps({"w4a16": w4a16_bench(log, s, W.prompt_ids(s, args.prompt, seed=0), sched, K, args.warmup,
-                                                4096)}), flush=True)
+        print(json.dumps({"w4a16": w4a16_bench(log, s, W.prompt_ids(s, args.prompt, seed=0), sched, gen_cyc,
+                                                args.warmup, 4096)}), flush=True)
         return 0
     t0 = time.time()
     weights = W.make_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
     log(f"weights drawn in {time.time() - t0:.1f}s")
     prompt = W.prompt_ids(s, args.prompt, seed=0)
-    sched = W.forced_accept_schedule(8192, B, seed=0)
     if args.quadratic_only:
         print(json.dumps({"quadratic": quadratic_bench(log, s, weights, prompt, sched, args.warmup, 4096,
                                                        n_cyc=args.steps or 40)}), flush=True)
         return 0
-    K = args.steps
-    if K is None:
-        tot, K = 1, 0
-        while tot < args.gen_tokens:
-            tot += int(sched[K])
-            K += 1
+    K = args.steps if args.steps is not None else 3
+    if K < 1:
+        print("bench.py: --steps must be at least 1", file=sys.stderr)
+        return 2
     max_ctx = 4096 if args.prompt + args.gen_tokens + 2 * B <= 4096 else args.prompt + args.gen_tokens + 1024
     t0 = time.time()
-    model = Model(s, weights, max_seqs=2, max_block=B, max_context=max_ctx, max_rows=1024)
+    # sequences 0..K-1 hold the timed generations; sequence K the warm-up
+    model = Model(s, weights, max_seqs=K + 1, max_block=B, max_context=max_ctx, max_rows=1024)
     torch.cuda.synchronize()
     log(f"model uploaded + packed in {time.time() - t0:.1f}s ({model.weight_bytes / 1e9:.2f} GB)")
     dev = model.device
 
-    def run_cycles(seq, n_cyc, sched_vals, first):
+    def run_cycles(seq, n, sched_vals, first):
         run = SelfSpecRun(model, B, seq)
-        blocks = torch.empty((n_cyc, B), dtype=torch.int32, device=dev)
-        ars = torch.empty((n_cyc, B), dtype=torch.int32, device=dev)
+        blocks = torch.empty((n, B), dtype=torch.int32, device=dev)
+        ars = torch.empty((n, B), dtype=torch.int32, device=dev)
         anchor = first.data_ptr()
         Ls = []
-        for c in range(n_cyc):
+        for c in range(n):
             run.block, run.ar = blocks[c], ars[c]
             L = run.cycle(anchor, None if sched_vals is None else int(sched_vals[c]))
             Ls.append(L)
             anchor = ars[c].data_ptr() + 4 * (L - 1)
         return Ls, anchor
 
-    # warm-up on sequence 1
-    first = prefill(model, 1, prompt)
-    run_cycles(1, args.warmup, W.forced_accept_schedule(args.warmup, B, seed=1), first)
+    # warm-up: whole generations on sequence K
+    for _ in range(args.warmup):
+        model.seq_reset(K)
+        first = prefill(model, K, prompt)
+        run_cycles(K, gen_cyc, sched, first)
     torch.cuda.synchronize()
-    model.seq_reset(1)
+    model.seq_reset(K)
 
-    # headline: K forced cycles on sequence 0
-    first = prefill(model, 0, prompt)
+    # headline: K whole generations, each on its own sequence prefilled before the timed region
+    firsts = [prefill(model, q, prompt) for q in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    Ls, _ = run_cycles(0, K, sched[:K], first)
+    for q in range(K):
+        Ls, _ = run_cycles(q, gen_cyc, sched, firsts[q])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    tokens = int(sum(Ls))
-    value = tokens / wall
-    log(f"self-spec forced: {K} cycles, {tokens} tokens in {wall * 1e3:.1f} ms -> {value:.1f} tok/s")
+    assert sum(Ls) == tot - 1
+    decoded = K * (args.gen_tokens - 1)        # tokens 2..N of every generation (y1 is the prefill's)
+    value = decoded / wall
+    log(f"self-spec forced: {K} generations x {gen_cyc} cycles, {decoded} decoded tokens in {wall * 1e3:.1f} ms "
+        f"-> {value:.1f} tok/s")
+    for q in range(K):
+        model.seq_reset(q)
+    cyc_tokens = tot - 1                       # tokens committed by one generation's cycles (before truncation)
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K,
            "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (random-init N(0,0.02^2) bf16 weights, uniform random prompt ids, seed 0)",
-           "config": {"workload": "8B-shape decoder (36 layers, d 4096, 32/8 heads x 128, FFN 12288, vocab 151936), "
-                                  "single query, prompt 1024, self-speculation block 32, forced accept L~U{1..32} "
-                                  "seed 0, 2048 generated tokens",
-                      "prompt_len": args.prompt, "generated_tokens": tokens + 1, "block": B,
-                      "accept_schedule": "forced uniform {1..32}, seed 0"}}
+           "config": {"workload": f"8B-shape decoder (36 layers, d 4096, 32/8 heads x 128, FFN 12288, vocab 151936), "
+                                  f"single query, prompt {args.prompt}, self-speculation block 32, forced accept "
+                                  f"L~U{{1..32}} seed 0; one step = one whole {args.gen_tokens}-token generation "
+                                  f"({gen_cyc} draft+verify cycles, committed length {args.prompt} -> "
+                                  f"{args.prompt + tot - 1}), its prompt prefilled before the timed region",
+                      "prompt_len": args.prompt, "generated_tokens": args.gen_tokens,
+                      "decoded_tokens_per_step": args.gen_tokens - 1, "cycles_per_step": gen_cyc,
+                      "block": B, "accept_schedule": "forced uniform {1..32}, seed 0"}}
 
     if not args.no_extras:
         # per-kernel-class timing passes (HIP events on the model's stream)
@@ -388,8 +413,8 @@ def main() -> int:
         out["modes"] = {"selfspec_natural": {"cycles": 16, "tokens": int(sum(Ln)), "tok_per_s": round(sum(Ln) / t_nat, 1),
                                              "mean_accept": round(float(np.mean(Ln)), 3)},
                         "ar": {"tokens": 64, "tok_per_s": round(64 / t_ar, 1), "ms_per_token": round(t_ar / 64 * 1e3, 3)},
-                        "selfspec_forced": {"tok_per_s": round(value, 1), "mean_accept": round(tokens / K, 3),
-                                            "tpf": round(tokens / (2 * K), 3)},
+                        "selfspec_forced": {"tok_per_s": round(value, 1), "mean_accept": round(cyc_tokens / gen_cyc, 3),
+                                            "tpf": round(cyc_tokens / (2 * gen_cyc), 3)},
                         "prefill_1024_ms": round(t_pf * 1e3, 2)}
 
     # the memory-bound 4-bit decode pass runs before the compute-bound quadratic one
@@ -397,14 +422,14 @@ def main() -> int:
         model.close()
         model = None
         torch.cuda.empty_cache()
-        out["w4a16"] = w4a16_bench(log, s, prompt, sched, K, args.warmup, max_ctx)
+        out["w4a16"] = w4a16_bench(log, s, prompt, sched, gen_cyc, args.warmup, max_ctx, args.gen_tokens - 1)
     if not args.no_extras and not args.no_quadratic:
         if model is not None:
             model.close()
             model = None
         torch.cuda.empty_cache()
         out["quadratic"] = quadratic_bench(log, s, weights, prompt, sched, args.warmup, max_ctx,
-                                           linear_tpf=tokens / (2 * K))
+                                           linear_tpf=cyc_tokens / (2 * gen_cyc))
 
     if args.calib_copy:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
@@ -416,19 +441,25 @@ def main() -> int:
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = 1 << 30
         del src, dst
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(s, weights, prompt, tokens / K, log)
     if model is not None:
         model.close()
-    if args.batch14b:
-        del weights
+        model = None
+    torch.cuda.empty_cache()
+    if not args.no_extras and not args.no_3b:
+        out["model_3b"] = bench_3b(log)
         torch.cuda.empty_cache()
-        out["batch_14b"] = batch14b_bench(log)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(s, weights, prompt, sched, log)
+    if not args.no_extras and not args.no_batch14b:
+        del weights
+        import gc
+        gc.collect()
+        out["batch_14b"] = batch14b_bench(log, n_gen=args.batch14b_tokens)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx) -> dict:
+def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx, decoded=None) -> dict:
     """The headline workload with the decoder's matrices in 4 bits (group-wise
     int4 + bf16 scales; embedding and LM head bf16): forced self-spec rate,
     per-class kernel times and the 4-bit gate/up GEMM against HBM."""
@@ -470,7 +501,7 @@ def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx) -> dict:
     Ls = run_cycles(0, K, sched[:K], first)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tokens = int(sum(Ls))
+    tokens = int(sum(Ls)) if decoded is None else int(decoded)   # a whole generation: its truncated length
     log(f"w4a16 self-spec forced: {K} cycles, {tokens} tokens in {wall * 1e3:.1f} ms -> {tokens / wall:.1f} tok/s")
     # per-class timing on sequence 1
     model.seq_reset(0)
@@ -505,9 +536,11 @@ def w4a16_bench(log, s, prompt, sched, K, warmup, max_ctx) -> dict:
     f_us = per["forward"]["avg_us"]
     fb = forward_bytes(s, int(statistics.mean(ns[-n_cyc:])), B, w4=True)
     ach = gu["bytes"] / (gu["avg_us"] * 1e-6) / 1e9
-    return {"workload": "the headline workload (8B shape, prompt 1024, block 32, forced accept U{1..32} seed 0) "
-                        "with QKV, O, gate/up and down as group-wise int4 + bf16 scales (group 128)",
-            "tok_per_s": round(tokens / wall, 1), "ms_per_step": round(wall * 1e3 / K, 4), "steps": K,
+    return {"workload": "the headline workload (8B shape, prompt 1024, block 32, forced accept U{1..32} seed 0; "
+                        f"one whole generation of {K} cycles, {tokens} decoded tokens) with QKV, O, gate/up and "
+                        "down as group-wise int4 + bf16 scales (group 128)",
+            "tok_per_s": round(tokens / wall, 1), "ms_per_cycle": round(wall * 1e3 / K, 4), "cycles": K,
+            "decoded_tokens": tokens,
             "kernels": per,
             "forward": {"avg_us": f_us, "algorithmic_bytes": fb, "hbm_frac": round(fb / (f_us * 1e-6) / 8e12, 4)},
             "roofline_gate_up": {"bound": "hbm", "kernel": "k_gemm_w4<EPI_SWIGLU>, M=32", "achieved": round(ach, 1),
@@ -677,16 +710,20 @@ def attention_op_bench(log) -> dict:
     return out
 
 
-def batch14b_bench(log) -> dict:
+def batch14b_bench(log, n_gen: int = 1024) -> dict:
     """The 14B-shaped batched diffusion workload: 16 sequences, prompt lengths
     uniform over {1024..8192} (seed 0), 64-token pages, block 32, tau 0.9 and at
-    most 8 denoising steps.  One block: every step and the causal commit
-    forward (M = 512 rows) timed with HIP events; each forward's algorithmic
-    HBM bytes (weights + KV read + KV written) and GEMM + attention flops
-    against the 8 TB/s and 2.5 PF/s (dense bf16) peaks."""
+    most 8 denoising steps, n_gen generated tokens per sequence (every
+    sequence's blocks in lockstep: up to 8 batched 512-row bidirectional
+    forwards, then one batched causal commit forward per block).  The whole
+    generation is timed from the end of the prefill; the first block's
+    forwards are also timed one by one with HIP events, each against its
+    algorithmic HBM bytes (weights + KV read + KV written) and its GEMM +
+    attention flops (8 TB/s and 2.5 PF/s dense bf16 peaks)."""
     import numpy as np
     import torch
     import workloads as W
+    from self_speculative_amd import decode as D
     from self_speculative_amd.decode import prefill
     from self_speculative_amd.model import Model
     s = W.SHAPES["14b"]
@@ -695,7 +732,8 @@ def batch14b_bench(log) -> dict:
     w = W.make_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
     lens = W.prompt_lengths(NSEQ, 1024, 8192, seed=0)
     prompts = [W.prompt_ids(s, int(n), seed=0, index=i) for i, n in enumerate(lens)]
-    model = Model(s, w, max_seqs=NSEQ, max_block=B, max_context=8192 + 2 * B, max_rows=NSEQ * B, free_host=True)
+    model = Model(s, w, max_seqs=NSEQ, max_block=B, max_context=8192 + n_gen + 2 * B, max_rows=NSEQ * B,
+                  free_host=True)
     del w
     torch.cuda.synchronize()
     log(f"14b batch: weights drawn and uploaded in {time.time() - t0:.1f}s")
@@ -706,6 +744,7 @@ def batch14b_bench(log) -> dict:
     torch.cuda.synchronize()
     t_pf = time.perf_counter() - t0
     seqs = list(range(NSEQ))
+    # the first block, forward by forward (HIP events)
     blk = torch.full((NSEQ, B), s.mask_id, dtype=torch.int32, device=dev)
     nm = torch.empty(NSEQ, dtype=torch.int32, device=dev)
     ar = torch.empty((NSEQ, B), dtype=torch.int32, device=dev)
@@ -729,6 +768,14 @@ def batch14b_bench(log) -> dict:
     t_blk = time.perf_counter() - t0
     assert int((blk == s.mask_id).sum().item()) == 0
     fwd_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    # the rest of the generation: whole blocks in lockstep, timed together
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gens = D.generate_diffusion_batch(model, prompts, n_gen - B, B, TAU, S_MAX, seqs, prefilled=True)
+    torch.cuda.synchronize()
+    t_rest = time.perf_counter() - t0
+    t_gen = t_blk + t_rest
+    n_fwd = len(fwd_us) + gens[0].forwards
     wbytes = sum(layer_weight_bytes(s).values()) * s.n_layers + s.vocab * s.d_model * 2
     kv_tok = s.n_layers * 2 * s.n_kv_heads * s.head_dim * 2
     M = NSEQ * B
@@ -738,30 +785,134 @@ def batch14b_bench(log) -> dict:
     attn_flops = 4 * sum(int(n) + B for n in lens) * B * s.n_q_heads * s.head_dim * s.n_layers
     flops = 2 * M * params + attn_flops
     med = float(np.median(fwd_us))
+    tokens = NSEQ * n_gen
     out = {"workload": "14B-shape decoder (40 layers, d 5120, 40/8 heads x 128, FFN 17408, vocab 151936), 16 sequences, "
-                       "prompt lengths U{1024..8192} seed 0, block 32, tau 0.9, at most 8 steps",
+                       f"prompt lengths U{{1024..8192}} seed 0, block 32, tau 0.9, at most 8 steps, {n_gen} generated "
+                       "tokens per sequence; decode timed from the end of the prefill",
            "prompt_tokens": int(lens.sum()), "prefill_s": round(t_pf, 3),
            "prefill_tok_per_s": round(float(lens.sum()) / t_pf, 1),
-           "forward_us": {"median": round(med, 1), "min": round(min(fwd_us), 1), "max": round(max(fwd_us), 1),
-                          "n": len(fwd_us)},
-           "forward_bytes": nbytes, "forward_flops": flops,
+           "generated_tokens": tokens, "forwards": n_fwd, "decode_s": round(t_gen, 3),
+           "tokens_per_s": round(tokens / t_gen, 1), "ms_per_forward": round(t_gen / n_fwd * 1e3, 2),
+           "first_block_forward_us": {"median": round(med, 1), "min": round(min(fwd_us), 1),
+                                      "max": round(max(fwd_us), 1), "n": len(fwd_us)},
+           "forward_bytes_first_block": nbytes, "forward_flops_first_block": flops,
            "hbm_frac": round(nbytes / (med * 1e-6) / 8e12, 4),
-           "mfma_frac": round(flops / (med * 1e-6) / 2.5e15, 4),
-           "block_s": round(t_blk, 4),
-           "tokens_per_s": round(NSEQ * B / t_blk, 1)}
-    log(f"14b batch: forward median {med:.0f} us, HBM {out['hbm_frac']:.3f}, MFMA {out['mfma_frac']:.3f}, "
-        f"{out['tokens_per_s']} tok/s, prefill {out['prefill_tok_per_s']} tok/s")
+           "mfma_frac": round(flops / (med * 1e-6) / 2.5e15, 4)}
+    log(f"14b batch: forward median {med:.0f} us, HBM {out['hbm_frac']:.3f}, MFMA {out['mfma_frac']:.3f}; "
+        f"{tokens} tokens in {t_gen:.2f}s -> {out['tokens_per_s']} tok/s, prefill {out['prefill_tok_per_s']} tok/s")
     model.close()
     return out
 
 
-def cpu_baseline(s, weights, prompt, tokens_per_cycle, log) -> dict:
-    """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    prefill of the first 32 prompt tokens (setup, untimed), then one
-    self-speculation cycle (bidirectional draft + causal verify of 32 rows)
-    timed; the rate is the headline's tokens per cycle over that cycle time."""
+def bench_3b(log, n_gen: int = 512, prompt_len: int = 512) -> dict:
+    """The 3B-shaped decoder (28 layers, d 3072, 24/8 heads x 128, FFN 8192,
+    vocab 151936), single query, a 512-token prompt and 512 generated tokens
+    with block 32: block diffusion (tau 0.9, no step cap: a block takes steps
+    until no MASK is left, then the causal commit forward), self-speculation
+    with the natural accept lengths, and AR.  Each mode's decode is timed from
+    the end of its prefill; forwards are also timed one by one with HIP events
+    (32-row bidirectional, 32-row causal) against the 3B forward's bytes."""
     import numpy as np
+    import torch
 
+    import workloads as W
+    from self_speculative_amd import decode as D
+    from self_speculative_amd.model import Model
+    s = W.SHAPES["3b"]
+    B = 32
+    t0 = time.time()
+    w = W.make_weights(s, seed=0, threads=min(16, len(os.sched_getaffinity(0))))
+    prompt = W.prompt_ids(s, prompt_len, seed=0)
+    model = Model(s, w, max_seqs=3, max_block=B, max_context=prompt_len + n_gen + 2 * B, max_rows=512,
+                  free_host=True)
+    del w
+    torch.cuda.synchronize()
+    log(f"3b: weights drawn and uploaded in {time.time() - t0:.1f}s")
+    dev = model.device
+    out = {"workload": f"3B-shape decoder (28 layers, d 3072, 24/8 heads x 128, FFN 8192, vocab 151936), single "
+                       f"query, prompt {prompt_len}, {n_gen} generated tokens, block 32; decode timed from the end of "
+                       f"the prefill"}
+    # warm-up
+    D.generate_ar(model, prompt, 8, seq=2)
+    model.seq_reset(2)
+    # block diffusion: tau 0.9 and no cap; the generation's forwards are timed one by one as well
+    first = D.prefill(model, 0, prompt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g = D.generate_diffusion_batch(model, [prompt], n_gen, B, 0.9, None, [0], prefilled=True)[0]
+    torch.cuda.synchronize()
+    t_diff = time.perf_counter() - t0
+    out["diffusion"] = {"tau": 0.9, "step_cap": None, "tokens": len(g.tokens), "forwards": g.forwards,
+                        "tpf": round(g.tpf, 3), "mean_steps_per_block": round(float(np.mean(g.steps_per_block)), 2),
+                        "tok_per_s": round(len(g.tokens) / t_diff, 1), "s": round(t_diff, 3)}
+    log(f"3b diffusion: {len(g.tokens)} tokens, {g.forwards} forwards in {t_diff:.2f}s -> "
+        f"{out['diffusion']['tok_per_s']} tok/s")
+    # self-speculation, natural accept lengths (one 4-byte read of L per cycle)
+    first = D.prefill(model, 1, prompt)
+    run = D.SelfSpecRun(model, B, 1)
+    blocks = torch.empty((n_gen, B), dtype=torch.int32, device=dev)
+    ars = torch.empty((n_gen, B), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    Ls, emitted, anchor = [], 1, first.data_ptr()
+    while emitted < n_gen:
+        run.block, run.ar = blocks[len(Ls)], ars[len(Ls)]
+        L = run.cycle(anchor, None)
+        anchor = ars[len(Ls)].data_ptr() + 4 * (L - 1)
+        Ls.append(L)
+        emitted += L
+    torch.cuda.synchronize()
+    t_ss = time.perf_counter() - t0
+    out["selfspec_natural"] = {"cycles": len(Ls), "decoded_tokens": n_gen - 1,
+                               "mean_accept": round(float(np.mean(Ls)), 3), "tpf": round((n_gen - 1) / (2 * len(Ls)), 3),
+                               "tok_per_s": round((n_gen - 1) / t_ss, 1), "s": round(t_ss, 3)}
+    log(f"3b self-spec: {len(Ls)} cycles (mean L {out['selfspec_natural']['mean_accept']}) in {t_ss:.2f}s -> "
+        f"{out['selfspec_natural']['tok_per_s']} tok/s")
+    # AR
+    model.seq_reset(0)
+    ar_out = torch.empty(n_gen, dtype=torch.int32, device=dev)
+    model.prefill(0, torch.as_tensor(prompt, device=dev), ar_out[0:1])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    base = ar_out.data_ptr()
+    for t in range(1, n_gen):
+        model.decode_ar(0, base + 4 * (t - 1), base + 4 * t)
+    torch.cuda.synchronize()
+    t_ar = time.perf_counter() - t0
+    out["ar"] = {"decoded_tokens": n_gen - 1, "tok_per_s": round((n_gen - 1) / t_ar, 1),
+                 "ms_per_token": round(t_ar / (n_gen - 1) * 1e3, 3)}
+    log(f"3b AR: {out['ar']['tok_per_s']} tok/s")
+    # per-forward latency at the end of the self-spec run (committed length ~ prompt + n_gen)
+    blk = torch.empty(B, dtype=torch.int32, device=dev)
+    ar = torch.empty(B, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    ev = []
+    for c in range(8):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        model.draft_block(1, anchor, B, blk)
+        e[1].record()
+        model.verify_block([1], blk, B, ar, acc)
+        e[2].record()
+        ev.append(e)
+    torch.cuda.synchronize()
+    n = model.seq_length(1)
+    fb = forward_bytes(s, n, B)
+    bid = _pct([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
+    cau = _pct([e[1].elapsed_time(e[2]) * 1e3 for e in ev])
+    out["forward"] = {"committed_len": n, "algorithmic_bytes": fb, "bidir_M32": bid, "causal_M32": cau,
+                      "hbm_frac": round(fb / (cau["median_us"] * 1e-6) / 8e12, 4)}
+    log(f"3b forward at n={n}: {cau['median_us']} us, HBM {out['forward']['hbm_frac']:.3f}")
+    model.close()
+    return out
+
+
+def cpu_baseline(s, weights, prompt, sched, log, n_cycles: int = 2) -> dict:
+    """The CPU oracle (as it stands) on a bounded sample of the headline job:
+    the same 1024-token prompt prefilled (setup, untimed), then the first
+    ``n_cycles`` cycles of the same forced schedule (a bidirectional draft and
+    a causal verify of 32 rows each, then the commit) timed at the headline's
+    committed length; the rate is those cycles' tokens over their time."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -772,18 +923,29 @@ def cpu_baseline(s, weights, prompt, tokens_per_cycle, log) -> dict:
     om = O.OracleModel(s, weights)
     sess = O.OracleSession(om, keep_logits=False)
     t0 = time.time()
-    first = sess.prefill(0, prompt[:32])
-    log(f"oracle setup (prefill 32, weight widening) {time.time() - t0:.1f}s")
+    first = sess.prefill(0, prompt)
+    t_setup = time.time() - t0
+    n0 = len(prompt)
+    log(f"oracle setup (weight widening, prefill {n0}) {t_setup:.1f}s")
+    g = int(first.tok[0])
+    toks = 0
     t0 = time.perf_counter()
-    blk, _ = sess.draft_block(0, int(first.tok[0]), 32)
-    sess.verify_block(0, blk)
+    for c in range(n_cycles):
+        L = int(sched[c])
+        blk, _ = sess.draft_block(0, g, 32)
+        a, _, _ = sess.verify_block(0, blk)
+        sess.commit_kv(0, L)
+        g = int(a[L - 1])
+        toks += L
     dt = time.perf_counter() - t0
-    log(f"oracle cycle {dt:.1f}s")
-    return {"value": round(tokens_per_cycle / dt, 4), "unit": "tokens/s", "cores": int(blas_threads or cores),
+    log(f"oracle {n_cycles} cycles ({toks} tokens) {dt:.1f}s")
+    return {"value": round(toks / dt, 4), "unit": "tokens/s", "cores": int(blas_threads or cores),
             "kind": "oracle",
-            "sample": f"one self-spec cycle (32-row bidirectional draft + 32-row causal verify, float64 NumPy, "
-                      f"36 layers) at committed length 32, {dt:.1f}s; rate = {tokens_per_cycle:.2f} tokens per "
-                      f"cycle (the headline schedule's mean) / cycle time; host has {cores} cores"}
+            "sample": f"the headline job's first {n_cycles} forced self-spec cycles (L = "
+                      f"{', '.join(str(int(v)) for v in sched[:n_cycles])}: {toks} tokens; each a 32-row "
+                      f"bidirectional draft + 32-row causal verify of the 36-layer 8B shape in float64 NumPy, then "
+                      f"the commit) at committed length {n0} -> {n0 + toks}, {dt:.1f}s; the {n0}-token prompt "
+                      f"prefilled first ({t_setup:.1f}s with the weight widening, untimed); host has {cores} cores"}
 
 
 if __name__ == "__main__":

@@ -1566,8 +1566,10 @@ __device__ __forceinline__ void part_push(SamplePart& a, float score, int v) {
   }
 }
 __device__ __forceinline__ void part_merge(SamplePart& a, const SamplePart& b) {
-  // b covers higher ids than a, so a wins ties
-  if (b.best > a.best) {
+  // the higher score wins, the lower id on equal scores: a thread's 4-id
+  // chunks interleave with the other threads', so the merge order says
+  // nothing about which part holds the lower ids
+  if (b.best > a.best || (b.best == a.best && b.idx < a.idx)) {
     a.second = fmaxf(a.best, b.second);
     a.best = b.best;
     a.idx = b.idx;

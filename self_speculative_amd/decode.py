@@ -169,14 +169,16 @@ def generate_selfspec_quadratic(model: Model, prompt, n_tokens: int, B: int,
 
 def generate_diffusion_batch(model: Model, prompts: Sequence, n_tokens: int, B: int, tau: float,
                              max_steps: Optional[int] = None, seqs: Optional[Sequence[int]] = None,
-                             tau_revise: Optional[float] = None) -> List[GpuGen]:
+                             tau_revise: Optional[float] = None, prefilled: bool = False) -> List[GpuGen]:
     """Block diffusion for several sequences in lockstep per block; with
     ``tau_revise`` each step also rewrites written positions
-    (``sdm_diffuse_step_revise``)."""
+    (``sdm_diffuse_step_revise``).  ``prefilled``: the sequences already hold
+    their prompts (the prefill is not repeated)."""
     dev = model.device
     seqs = list(seqs) if seqs is not None else list(range(len(prompts)))
-    for s, p in zip(seqs, prompts):
-        prefill(model, s, p)
+    if not prefilled:
+        for s, p in zip(seqs, prompts):
+            prefill(model, s, p)
     mask = model.shape.mask_id
     n = len(seqs)
     out = [GpuGen([], 0) for _ in seqs]

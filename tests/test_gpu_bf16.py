@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from lockstep import MARGIN_EXEMPT, Report, tokens_agree
+from lockstep import Report, accept_exempt, tokens_agree
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +67,7 @@ def test_bf16_lockstep_selfspec_and_ar(gm, om):
         gblk = blk.cpu().numpy()
         assert tokens_agree(np.r_[0, gblk[1:]], osel, range(1, B), rep), rep.notes
         if not np.array_equal(gblk, oblk):
-            rep.resyncs += 1
+            rep.resync()
             blk.copy_(_i32(oblk))
         gm.verify_block([seq], blk, B, ar, acc, lg)
         oa, oL, vsel = sess.verify_block(0, oblk)
@@ -76,8 +76,8 @@ def test_bf16_lockstep_selfspec_and_ar(gm, om):
         assert tokens_agree(ar.cpu().numpy(), vsel, range(B), rep), rep.notes
         gL = int(acc.item())
         if gL != oL:
-            assert np.any(vsel.margin[: max(gL, oL)] < MARGIN_EXEMPT)
-            rep.resyncs += 1
+            assert accept_exempt(vsel, gL, oL, rep), rep.notes
+            rep.resync()
         L = [oL, 17, 32, 1][cyc]                  # natural L first, then forced lengths
         gm.commit_kv(seq, L)
         sess.commit_kv(0, L)
@@ -89,8 +89,8 @@ def test_bf16_lockstep_selfspec_and_ar(gm, om):
         rep.logits(lg[:1], r.logits)
         assert tokens_agree(nxt.cpu().numpy(), r, [0], rep), rep.notes
         g = int(r.tok[0])
-    print(f"bf16 lockstep: max|dlogit| {rep.max_logit_err:.3e}, tokens {rep.compared_tokens}, "
-          f"exempt {rep.exempt}, resyncs {rep.resyncs}", flush=True)
+    print(f"bf16 lockstep: {rep.summary()}", flush=True)
+    rep.assert_strict()
     assert rep.max_logit_err <= 2e-2
 
 
@@ -122,7 +122,8 @@ def test_bf16_lockstep_diffusion(gm, om):
         if not np.array_equal(got, new):
             from lockstep import unmask_exempt
             assert unmask_exempt(blk, sel, tau, SHAPE.mask_id), (got, new)
-            rep.resyncs += 1
+            rep.exempt += 1
+            rep.resync()
         else:
             assert int(nm.item()) == left
         blk = new
@@ -133,7 +134,8 @@ def test_bf16_lockstep_diffusion(gm, om):
     sess.verify_block(0, blk)
     gm.commit_kv(seq, B)
     sess.commit_kv(0, B)
-    print(f"bf16 diffusion lockstep: max|dlogit| {rep.max_logit_err:.3e}, resyncs {rep.resyncs}", flush=True)
+    print(f"bf16 diffusion lockstep: {rep.summary()}", flush=True)
+    rep.assert_strict()
     assert rep.max_logit_err <= 2e-2
 
 
@@ -169,14 +171,15 @@ def test_bf16_lockstep_diffusion_with_revision(gm, om):
             masked = blk == SHAPE.mask_id
             assert (not masked[diff].all() or unmask_exempt(blk, sel, tau, SHAPE.mask_id, eps)), (got, new)
             assert revise_exempt(blk, sel, taur, SHAPE.mask_id, eps, diff[~masked[diff]]), (got, new)
-            rep.resyncs += 1
+            rep.exempt += 1
+            rep.resync()
         else:
             assert int(nm.item()) == left and int(nr.item()) == len(R)
         revised += len(R)
         blk = new
     assert (blk != SHAPE.mask_id).all() and revised > 0
-    print(f"bf16 revision lockstep: max|dlogit| {rep.max_logit_err:.3e}, revised {revised}, resyncs {rep.resyncs}",
-          flush=True)
+    print(f"bf16 revision lockstep: revised {revised}, {rep.summary()}", flush=True)
+    rep.assert_strict()
     assert rep.max_logit_err <= 2e-2
 
 
@@ -326,6 +329,26 @@ def test_bf16_streamed_attention_matches_tile_parallel(weights):
         m.diffuse_step([i], b1, B, 0.9, False, nm[:1], None, l1)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(l1.cpu().numpy(), batch[i * B:(i + 1) * B])
+    m.close()
+
+
+def test_bf16_decode_forward_repeatable(weights):
+    """The same 32-row forward, repeated, gives the same bits every time (one
+    sequence of 1900 keys: 8 attention splits per KV head, split-K GEMMs):
+    nothing in the decode path depends on which workgroup finishes first."""
+    from self_speculative_amd.model import Model
+    m = Model(SHAPE, weights, max_seqs=1, max_block=B, max_context=2048, max_rows=B)
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    m.prefill(0, _i32(W.prompt_ids(SHAPE, 1900, seed=35)), nxt)
+    blk = torch.empty(B, dtype=torch.int32, device=DEV)
+    lg = torch.empty((B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+    m.draft_block(0, nxt, B, blk, lg)
+    torch.cuda.synchronize()
+    ref = lg.clone()
+    for r in range(40):
+        m.draft_block(0, nxt, B, blk, lg)
+        torch.cuda.synchronize()
+        assert torch.equal(lg, ref), r
     m.close()
 
 

@@ -3,22 +3,25 @@
 * 8B (36 layers, d 4096, 32/8 heads, FFN 12288, vocab 151936) in exactly the
   launch configuration bench.py times (prompt 1024 in one 1024-row prefill
   chunk, 32-row blocks): prefill, a draft, a verify, a commit and an AR step in
-  lockstep with the float64 oracle -- every logit of every row compared.
+  lockstep with the float64 oracle -- every logit of every row compared; then
+  a second sequence with a 2100-token prompt, so that self-speculation cycles
+  and an AR step run at committed lengths above 2048.
 * 3B (28 layers): self-speculation and block diffusion windows in lockstep.
-* 14B width: oracle lockstep on the shape truncated to 2 layers (the per-layer
-  kernels and their launch configuration are those of the full model), and on
-  the full 40-layer model a property that holds at any size: a batch of 16
-  sequences with prompt lengths in [1024, 8192] (64-token pages) gives each
-  sequence the same bits as running it alone.
+* 14B at full depth (40 layers): two sequences prefilled and one batched
+  diffusion step in lockstep, every row's logits compared; 14B width over two
+  layers; and on the full model with the 16-sequence batch of prompt lengths
+  in [1024, 8192] (64-token pages), each sequence's bits equal to running it
+  alone.
 
-Logits must agree within 2e-2 (max abs).  Token, accept and unmask decisions
-must agree except where the oracle's decision is closer to a tie than the
-row's own measured logit deviation can move it (never below the 1e-3 margin
-rule): with every logit of a row within eps of the oracle, an argmax can only
-differ when the oracle's top-2 margin is below 2 eps.  At these depths fp32
-summation alone (the oracle run in float32 against itself in float64) moves
-logits by about 1e-2, so a flat 1e-3 rule would test summation order, not the
-kernels.
+Logits must agree within 2e-2 (max abs); at 14B full depth within 1.5 x the
+oracle's own float32-vs-float64 gap on the same inputs (2.08e-2, above 2e-2:
+no fp32 implementation can meet 2e-2 there).  Token, accept and unmask decisions
+must agree exactly except where the oracle's decision is a near-tie: top-2
+margin below 1e-3, or log-confidence within 1e-3 of the threshold or of the
+runner-up (the near-tie reading of the parity rule).  Every resync must follow
+such an exempt decision.  The summary also counts agreed decisions whose
+oracle margin lay within twice the row's measured logit deviation (a
+diagnostic of how close the run came to a flip).
 """
 import gc
 
@@ -28,12 +31,16 @@ import torch
 
 import oracle as O
 import workloads as W
-from lockstep import MARGIN_EXEMPT, Report, tokens_agree, unmask_exempt
+from lockstep import Report, accept_exempt, tokens_agree, unmask_exempt
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 B = 32
 LOGIT_TOL = 2e-2
+# 14B at full depth: the oracle run in float32 differs from itself in float64
+# by 2.08e-2 on this test's inputs (tests/oracle_fp32_floor.py), so no fp32
+# implementation can meet 2e-2 there; the bar is 1.5 x that measured floor.
+LOGIT_TOL_14B_FULL = 1.5 * 2.08e-2
 
 
 def _i32(x):
@@ -53,7 +60,7 @@ def _lockstep_cycle(gm, sess, seq, g, L_forced, rep, lg):
     assert gb[0] == g
     assert tokens_agree(np.r_[0, gb[1:]], osel, range(1, B), rep, eps), rep.notes
     if not np.array_equal(gb, oblk):
-        rep.resyncs += 1
+        rep.resync()
         blk.copy_(_i32(oblk))
     gm.verify_block([seq], blk, B, ar, acc, lg)
     oa, oL, vsel = sess.verify_block(0, oblk)
@@ -62,11 +69,8 @@ def _lockstep_cycle(gm, sess, seq, g, L_forced, rep, lg):
     assert tokens_agree(ar.cpu().numpy(), vsel, range(B), rep, eps), rep.notes
     gL = int(acc.item())
     if gL != oL:
-        # the accept length is the first draft/argmax mismatch: it may differ
-        # only through an exempt argmax before it
-        k = min(gL, oL) - 1
-        assert vsel.margin[k] < max(MARGIN_EXEMPT, 2 * eps[k]), (gL, oL, vsel.margin[: max(gL, oL)])
-        rep.resyncs += 1
+        assert accept_exempt(vsel, gL, oL, rep), rep.notes
+        rep.resync()
     L = oL if L_forced is None else L_forced
     gm.commit_kv(seq, L)
     sess.commit_kv(0, L)
@@ -88,13 +92,15 @@ def _diffuse_lockstep(gm, sessions, seqs, blocks, tau, force, rep, lg, mask_id):
         eps = rep.logits(lg[i * B:(i + 1) * B], sel.logits)
         if not np.array_equal(got[i], new):
             assert unmask_exempt(out[i], sel, tau, mask_id, eps), (i, got[i], new)
-            rep.resyncs += 1
+            rep.exempt += 1
+            rep.resync()
         else:
             assert int(nm[i].item()) == left
         out[i] = new
     return out
 
 
+@pytest.mark.timeout(900)
 def test_8b_bench_configuration_lockstep():
     from self_speculative_amd.model import Model
     s = W.SHAPES["8b"]
@@ -123,14 +129,40 @@ def test_8b_bench_configuration_lockstep():
     torch.cuda.synchronize()
     eps = rep.logits(lg[:1], r.logits)
     assert tokens_agree(nxt.cpu().numpy(), r, [0], rep, eps), rep.notes
-    print(f"8b lockstep: max|dlogit| {rep.max_logit_err:.3e}, tokens {rep.compared_tokens}, exempt {rep.exempt}, "
-          f"resyncs {rep.resyncs}", flush=True)
+    print(f"8b lockstep: {rep.summary()}", flush=True)
+    rep.assert_strict()
     assert rep.max_logit_err <= LOGIT_TOL
+    # committed lengths above 2048: a 2100-token prompt (three prefill chunks),
+    # a natural and a forced cycle, then an AR step
+    p2 = W.prompt_ids(s, 2100, seed=0, index=1)
+    sess2 = O.OracleSession(om)
+    rep2 = Report()
+    print("8b: prefill 2100 on a second sequence (gpu, then oracle)", flush=True)
+    gm.prefill(1, _i32(p2), nxt, lg[:1])
+    ref = sess2.prefill(0, p2)
+    torch.cuda.synchronize()
+    eps = rep2.logits(lg[:1], ref.logits)
+    assert tokens_agree(nxt.cpu().numpy(), ref, [0], rep2, eps), rep2.notes
+    g = int(ref.tok[0])
+    for cyc, L in enumerate([None, 32]):
+        print(f"8b: self-spec cycle {cyc} at committed length {gm.seq_length(1)}", flush=True)
+        g = _lockstep_cycle(gm, sess2, 1, g, L, rep2, lg)
+    assert gm.seq_length(1) >= 2048 + 32
+    print(f"8b: AR step at committed length {gm.seq_length(1)}", flush=True)
+    gm.decode_ar(1, _i32([g]), nxt, lg[:1])
+    r = sess2.decode_ar(0, g)
+    torch.cuda.synchronize()
+    eps = rep2.logits(lg[:1], r.logits)
+    assert tokens_agree(nxt.cpu().numpy(), r, [0], rep2, eps), rep2.notes
+    print(f"8b lockstep above 2048: {rep2.summary()}", flush=True)
+    rep2.assert_strict()
+    assert rep2.max_logit_err <= LOGIT_TOL
     gm.close()
-    del om, sess, w
+    del om, sess, sess2, w
     gc.collect()
 
 
+@pytest.mark.timeout(900)
 def test_3b_selfspec_and_diffusion_windows():
     from self_speculative_amd.model import Model
     s = W.SHAPES["3b"]
@@ -159,10 +191,49 @@ def test_3b_selfspec_and_diffusion_windows():
         print(f"3b: diffusion step {st}", flush=True)
         blk = _diffuse_lockstep(gm, [sess2], [1], blk, 0.9, force, rep, lg, s.mask_id)
     assert (blk != s.mask_id).all()
-    print(f"3b lockstep: max|dlogit| {rep.max_logit_err:.3e}, tokens {rep.compared_tokens}, exempt {rep.exempt}, "
-          f"resyncs {rep.resyncs}", flush=True)
+    print(f"3b lockstep: {rep.summary()}", flush=True)
+    rep.assert_strict()
     assert rep.max_logit_err <= LOGIT_TOL
     gm.close()
+
+
+@pytest.mark.timeout(900)
+def test_14b_full_depth_lockstep():
+    """The 40-layer 14B shape against the float64 oracle: two sequences
+    (prompts of 257 and 600 tokens, each prefilled in one chunk), then one
+    batched diffusion step over both blocks (64 rows); the prefills' last-row
+    logits and every row of the step compared, and the unmask decisions."""
+    from self_speculative_amd.model import Model
+    s = W.SHAPES["14b"]
+    print("14b full depth: drawing weights", flush=True)
+    w = W.make_weights(s, seed=0)
+    lens = [257, 600]
+    prompts = [W.prompt_ids(s, n, seed=0, index=i) for i, n in enumerate(lens)]
+    gm = Model(s, w, max_seqs=2, max_block=B, max_context=1024, max_rows=640)
+    om = O.OracleModel(s, w)           # widened layers are kept: ~112 GB of float64 on the host
+    rep = Report()
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    lg = torch.empty((2 * B, s.vocab), dtype=torch.float32, device=DEV)
+    sessions = []
+    for i, p in enumerate(prompts):
+        print(f"14b full depth: prefill {len(p)} on sequence {i} (gpu, then oracle)", flush=True)
+        gm.prefill(i, _i32(p), nxt, lg[:1])
+        ss = O.OracleSession(om)
+        ref = ss.prefill(0, p)
+        torch.cuda.synchronize()
+        eps = rep.logits(lg[:1], ref.logits)
+        assert tokens_agree(nxt.cpu().numpy(), ref, [0], rep, eps), rep.notes
+        sessions.append(ss)
+    blk = np.full((2, B), s.mask_id, dtype=np.int32)
+    print("14b full depth: one batched diffusion step (64 rows)", flush=True)
+    blk = _diffuse_lockstep(gm, sessions, [0, 1], blk, 0.9, False, rep, lg, s.mask_id)
+    assert ((blk != s.mask_id).sum(axis=1) >= 1).all()
+    print(f"14b full depth lockstep: {rep.summary()}", flush=True)
+    rep.assert_strict()
+    assert rep.max_logit_err <= LOGIT_TOL_14B_FULL
+    gm.close()
+    del om, sessions, w
+    gc.collect()
 
 
 def test_14b_width_two_layer_lockstep():
@@ -187,7 +258,8 @@ def test_14b_width_two_layer_lockstep():
         print(f"14b-width: batched diffusion step {st}", flush=True)
         blk = _diffuse_lockstep(gm, sessions, [0, 1], blk, 0.9, force, rep, lg, s.mask_id)
     assert (blk != s.mask_id).all()
-    print(f"14b-width lockstep: max|dlogit| {rep.max_logit_err:.3e}, resyncs {rep.resyncs}", flush=True)
+    print(f"14b-width lockstep: {rep.summary()}", flush=True)
+    rep.assert_strict()
     assert rep.max_logit_err <= LOGIT_TOL
     gm.close()
 
@@ -222,6 +294,7 @@ def test_14b_width_batch_position_independence_one_layer():
     gm.close()
 
 
+@pytest.mark.timeout(900)
 def test_14b_batch16_independence():
     from self_speculative_amd.model import Model
     s = W.SHAPES["14b"]

@@ -123,3 +123,43 @@ def test_w4_selfspec_sample_stream():
     g = D.generate_selfspec_sample(gm, p, 60, 16, 0.9, seed, seq=0)
     gm.close()
     assert g.tokens == ref.tokens and g.accept_lengths == ref.accept_lengths
+
+
+def test_sampled_tie_goes_to_the_lowest_id():
+    """An exact tie of perturbed scores is resolved to the lowest id whatever
+    thread scans it.  A row's ids are scanned in 4-id chunks handed to the
+    threads round robin, so ids 4..7 (thread 1's first chunk) are lower than
+    ids 1024..1027 (thread 0's second chunk of the same part).  LM-head rows 4
+    and 1024 are set to 4096 x the row of the greedy token: both logits are
+    then exactly 4096 x its logit (a power of two scales every product), and
+    at T = 1e-6 a perturbed score above 4e8 absorbs the Gumbel noise
+    (|g| < 18, below half a unit in the last place), so the two scores tie
+    exactly in fp32.  The float64 oracle sees no tie there (its sum keeps the noise), so
+    the rule itself is the reference."""
+    from self_speculative_amd.model import Model
+    s = W.ModelShape("tie-bf16", 1, 128, 1, 1, 128, 256, 151936, "bf16")
+    w = W.make_weights(s, seed=5)
+    p = torch.as_tensor(W.prompt_ids(s, 9, seed=5), device=DEV)
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    lg = torch.empty((1, s.vocab), dtype=torch.float32, device=DEV)
+    m = Model(s, w, max_seqs=1, max_block=8, max_context=64, max_rows=16)
+    m.prefill(0, p, nxt, lg)
+    torch.cuda.synchronize()
+    j = int(nxt.item())
+    top = float(lg[0, j].item())
+    m.close()
+    assert top > 0.1
+    row = W.f32_from_bf16_bits(w["lm_head"][j]) * np.float32(4096.0)
+    lo, hi = 4, 1024
+    for planted, expect in (((hi,), hi), ((lo, hi), lo)):
+        w2 = dict(w)
+        w2["lm_head"] = w["lm_head"].copy()
+        for v in planted:
+            w2["lm_head"][v] = W.bf16_bits_from_f32(row)
+        m = Model(s, w2, max_seqs=1, max_block=8, max_context=64, max_rows=16)
+        for seed in (1, 2, 3):
+            m.seq_reset(0)
+            m.prefill_sample(0, p, 1e-6, seed, nxt)
+            torch.cuda.synchronize()
+            assert int(nxt.item()) == expect, (planted, seed, int(nxt.item()))
+        m.close()
