@@ -321,6 +321,29 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
                          const void* d_pool, const int32_t* d_pages, int32_t n_prefix, int32_t T, int32_t mode,
                          void* d_out, void* d_workspace, size_t ws_bytes, void* hip_stream);
 
+/* ---- allocation-free attention ---------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as sdm_attention, with the same arguments except the workspace.
+ * Its per-split partials live in a device array of the library,
+ * sdm_attention_scratch_max_bytes() bytes (16 MiB) on every device the library
+ * runs on, held from the moment the library's code is loaded on that device
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * library allocation); the scratch address is looked up once per device, on
+ * the first call made with that device current.
+ * Limits and errors: as sdm_attention, plus SDM_ERR_CAPACITY (nothing
+ * enqueued) when the partials, sdm_attn_workspace_bytes(n_q_heads, n_kv_heads,
+ * head_dim, T, n_prefix + T), exceed the scratch (32 q / 8 KV heads, T = 32:
+ * up to 7936 keys).  The stream must belong to the current device.  Every
+ * call on a device shares that device's scratch and every partial is written
+ * before it is read, so nothing needs clearing between calls; calls that
+ * overlap on one device (concurrent streams, or host threads) race on the
+ * scratch and must be serialised by the caller. */
+size_t sdm_attention_scratch_max_bytes(void);
+sdm_status sdm_attention_noalloc(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const void* d_q,
+                                 const void* d_pool, const int32_t* d_pages, int32_t n_prefix, int32_t T,
+                                 int32_t mode, void* d_out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

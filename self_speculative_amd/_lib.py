@@ -87,6 +87,9 @@ SIGNATURES = {
     "sdm_attn_pack_kv": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "sdm_attention": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
+    "sdm_attention_scratch_max_bytes": (c_size_t, []),
+    "sdm_attention_noalloc": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                        c_int32, c_void_p, c_void_p]),
 }
 
 _lib = None

@@ -335,4 +335,10 @@ hipError_t launch_set_ints(int* dst, const int* vals, int n, hipStream_t st);   
 hipError_t launch_attn_pack_kv(int Hkv, const uint16_t* k, const uint16_t* v, int n_keys, const int* pages,
                                uint16_t* pool, hipStream_t st);
 
+// Allocation-free attention: the device scratch array's address on the
+// current device (looked up once per device, then cached).
+constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t attn_scratch_address(void** out);
+
 }  // namespace sdm

@@ -19,6 +19,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.hpp"
 #include "placement.hpp"
@@ -1424,7 +1425,38 @@ hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.
+// ---------------------------------------------------------------------------
+// Device-resident scratch of the allocation-free attention entry point: the
+// attention partials (per split O, max and sum) live in this array instead of
+// a caller workspace.  Each device holds its own copy from the moment the code
+// object is loaded on it until the process ends.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t attn_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    // the array's device address on the current device (the name itself is a
+    // host-side stand-in that no kernel may be given)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.
 __global__ void k_attn_pack_kv(int Hkv, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_keys,
                                const int* __restrict__ pages, uint16_t* __restrict__ pool) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -1074,20 +1074,29 @@ sdm_status sdm_attn_pack_kv(int32_t n_kv_heads, int32_t head_dim, const void* d_
   return SDM_OK;
 }
 
-sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const void* d_q, const void* d_pool,
-                         const int32_t* d_pages, int32_t n_prefix, int32_t T, int32_t mode, void* d_out,
-                         void* d_workspace, size_t ws_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+// Checks shared by both attention entry points (before anything is enqueued).
+sdm_status attention_check(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const void* d_q,
+                           const void* d_pool, const int32_t* d_pages, int32_t n_prefix, int32_t T, int32_t mode,
+                           const void* d_out) {
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads) return fail(SDM_ERR_UNSUPPORTED, "bad head counts");
   if (head_dim != kHd) return fail(SDM_ERR_UNSUPPORTED, "attention op needs head_dim %d", kHd);
-  if (!d_q || !d_pool || !d_pages || !d_out || !d_workspace) return fail(SDM_ERR_ARG, "null pointer");
+  if (!d_q || !d_pool || !d_pages || !d_out) return fail(SDM_ERR_ARG, "null pointer");
   if (n_prefix < 0 || T < 1 || T > 4096) return fail(SDM_ERR_ARG, "bad n_prefix / T");
   if ((int64_t)n_prefix + T > 65536) return fail(SDM_ERR_UNSUPPORTED, "more than 65536 keys");
   if (mode != SDM_CAUSAL && mode != SDM_BIDIR) return fail(SDM_ERR_ARG, "bad mode");
+  return SDM_OK;
+}
+
+// The attention op with its partials in ws (at least attn_ws_layout bytes).
+sdm_status attention_run(int32_t n_q_heads, int32_t n_kv_heads, const void* d_q, const void* d_pool,
+                         const int32_t* d_pages, int32_t n_prefix, int32_t T, int32_t mode, void* d_out, char* ws,
+                         void* hip_stream) {
   int64_t off_ml;
-  const int64_t need = attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml);
-  if ((int64_t)ws_bytes < need) return fail(SDM_ERR_CAPACITY, "attention workspace too small");
+  attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml);
   hipStream_t st = (hipStream_t)hip_stream;
-  char* ws = (char*)d_workspace;
   const int32_t nkeys = n_prefix + T;
   hipError_t e = hipSuccess;
   AttnArgs aa{};
@@ -1119,6 +1128,41 @@ sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim
   if (e == hipSuccess) e = launch_attn_combine_bf16(aa, st);
   if (e != hipSuccess) return fail(SDM_ERR_DEVICE, "attention: %s", hipGetErrorString(e));
   return SDM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+sdm_status sdm_attention(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const void* d_q, const void* d_pool,
+                         const int32_t* d_pages, int32_t n_prefix, int32_t T, int32_t mode, void* d_out,
+                         void* d_workspace, size_t ws_bytes, void* hip_stream) {
+  sdm_status s = attention_check(n_q_heads, n_kv_heads, head_dim, d_q, d_pool, d_pages, n_prefix, T, mode, d_out);
+  if (s != SDM_OK) return s;
+  if (!d_workspace) return fail(SDM_ERR_ARG, "null pointer");
+  int64_t off_ml;
+  const int64_t need = attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml);
+  if ((int64_t)ws_bytes < need) return fail(SDM_ERR_CAPACITY, "attention workspace too small");
+  return attention_run(n_q_heads, n_kv_heads, d_q, d_pool, d_pages, n_prefix, T, mode, d_out, (char*)d_workspace,
+                       hip_stream);
+}
+
+size_t sdm_attention_scratch_max_bytes(void) { return kAttnScratchBytes; }
+
+sdm_status sdm_attention_noalloc(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const void* d_q,
+                                 const void* d_pool, const int32_t* d_pages, int32_t n_prefix, int32_t T,
+                                 int32_t mode, void* d_out, void* hip_stream) {
+  sdm_status s = attention_check(n_q_heads, n_kv_heads, head_dim, d_q, d_pool, d_pages, n_prefix, T, mode, d_out);
+  if (s != SDM_OK) return s;
+  int64_t off_ml;
+  const int64_t need = attn_ws_layout(n_q_heads, n_kv_heads, T, n_prefix + T, &off_ml);
+  if (need > (int64_t)kAttnScratchBytes)
+    return fail(SDM_ERR_CAPACITY, "attention partials need %lld bytes, the device scratch holds %zu",
+                (long long)need, kAttnScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = attn_scratch_address(&scratch);
+  if (e != hipSuccess) return fail(SDM_ERR_DEVICE, "scratch address: %s", hipGetErrorString(e));
+  return attention_run(n_q_heads, n_kv_heads, d_q, d_pool, d_pages, n_prefix, T, mode, d_out, (char*)scratch,
+                       hip_stream);
 }
 
 }  // extern "C"
