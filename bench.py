@@ -191,13 +191,18 @@ def main() -> int:
 
     # headline: K whole generations, each on its own sequence prefilled before the timed region
     firsts = [prefill(model, q, prompt) for q in range(K)]
+    gen_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    gen_ev[0].record()
     for q in range(K):
         Ls, _ = run_cycles(q, gen_cyc, sched, firsts[q])
+        gen_ev[q + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    gen_ms = [gen_ev[q].elapsed_time(gen_ev[q + 1]) for q in range(K)]
+    log("generation ms (GPU events): " + " ".join(f"{v:.1f}" for v in gen_ms))
     assert sum(Ls) == tot - 1
     decoded = K * (args.gen_tokens - 1)        # tokens 2..N of every generation (y1 is the prefill's)
     value = decoded / wall
