@@ -1456,7 +1456,7 @@ hipError_t attn_scratch_address(void** out) {
   return hipSuccess;
 }
 
-// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.
+// Scatter row-major K/V [n_keys][Hkv][128] into single-layer pages.
 __global__ void k_attn_pack_kv(int Hkv, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_keys,
                                const int* __restrict__ pages, uint16_t* __restrict__ pool) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
