@@ -4,8 +4,9 @@
   launch configuration bench.py times (prompt 1024 in one 1024-row prefill
   chunk, 32-row blocks): prefill, a draft, a verify, a commit and an AR step in
   lockstep with the float64 oracle -- every logit of every row compared; then
-  a second sequence with a 2100-token prompt, so that self-speculation cycles
-  and an AR step run at committed lengths above 2048.
+  a second sequence with a 3000-token prompt, so that self-speculation cycles
+  and an AR step run at the end of the bench's committed-length range (1024 ->
+  3086).
 * 3B (28 layers): self-speculation and block diffusion windows in lockstep.
 * 14B at full depth (40 layers): two sequences prefilled and one batched
   diffusion step in lockstep, every row's logits compared; 14B width over two
@@ -132,12 +133,12 @@ def test_8b_bench_configuration_lockstep():
     print(f"8b lockstep: {rep.summary()}", flush=True)
     rep.assert_strict()
     assert rep.max_logit_err <= LOGIT_TOL
-    # committed lengths above 2048: a 2100-token prompt (three prefill chunks),
-    # a natural and a forced cycle, then an AR step
-    p2 = W.prompt_ids(s, 2100, seed=0, index=1)
+    # committed lengths at the end of the bench's range: a 3000-token prompt
+    # (three prefill chunks), a natural and a forced cycle, then an AR step
+    p2 = W.prompt_ids(s, 3000, seed=0, index=1)
     sess2 = O.OracleSession(om)
     rep2 = Report()
-    print("8b: prefill 2100 on a second sequence (gpu, then oracle)", flush=True)
+    print("8b: prefill 3000 on a second sequence (gpu, then oracle)", flush=True)
     gm.prefill(1, _i32(p2), nxt, lg[:1])
     ref = sess2.prefill(0, p2)
     torch.cuda.synchronize()
@@ -147,14 +148,14 @@ def test_8b_bench_configuration_lockstep():
     for cyc, L in enumerate([None, 32]):
         print(f"8b: self-spec cycle {cyc} at committed length {gm.seq_length(1)}", flush=True)
         g = _lockstep_cycle(gm, sess2, 1, g, L, rep2, lg)
-    assert gm.seq_length(1) >= 2048 + 32
+    assert gm.seq_length(1) >= 3000 + 33
     print(f"8b: AR step at committed length {gm.seq_length(1)}", flush=True)
     gm.decode_ar(1, _i32([g]), nxt, lg[:1])
     r = sess2.decode_ar(0, g)
     torch.cuda.synchronize()
     eps = rep2.logits(lg[:1], r.logits)
     assert tokens_agree(nxt.cpu().numpy(), r, [0], rep2, eps), rep2.notes
-    print(f"8b lockstep above 2048: {rep2.summary()}", flush=True)
+    print(f"8b lockstep at committed lengths 3000-3070: {rep2.summary()}", flush=True)
     rep2.assert_strict()
     assert rep2.max_logit_err <= LOGIT_TOL
     gm.close()
