@@ -71,18 +71,29 @@ def kernel_bytes(s, cls: str, M: int, w4: bool = False) -> int:
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_gemm_8b_selfspec_hbm_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "self_speculative_amd", "csrc", "sdm_kernels.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "self_speculative_amd", "build.py")
+
+
+def kernel_build_sha256() -> str:
+    """sha256 of the kernel source followed by the build script (its compiler flags)."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, BUILD_SCRIPT):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
-    --pmc record, or None if the kernel source changed since it was taken."""
-    import hashlib
+    --pmc record, or None if the kernel source or its build flags changed
+    since it was taken."""
     try:
         kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_RECORD) if "=" in l and not l.startswith("#"))
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        sha = kernel_build_sha256()
     except OSError:
         return None
-    if kv.get("kernel_source_sha256") != sha:
+    if kv.get("kernel_build_sha256") != sha:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 

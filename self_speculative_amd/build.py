@@ -34,6 +34,10 @@ def build(verbose: bool = False) -> str:
            # epilogue (one per activation-tile count) then rounds identically,
            # so a row's result does not depend on the batch it is computed in
            "-ffp-contract=off",
+           # MFMA accumulators in VGPRs: the attention's softmax rescale and
+           # the GEMM epilogues then work on them without AGPR copies (same
+           # instructions and results, fewer moves)
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"),
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
     if verbose:
