@@ -247,8 +247,8 @@ struct AttnArgs {
   Slots slots;
   int Hq, mode;
   float scale;
-  float* opart;          // [slots][Hkv][max_splits][nq_pad][hd]
-  float* mlpart;         // [slots][Hkv][max_splits][nq_pad][2]
+  float* opart;          // [slots][Hkv][max_splits][hd / 4][nq_pad] float4s
+  float* mlpart;         // [slots][Hkv][max_splits][2][nq_pad]: max, then sum
   int max_splits, nq_pad;
   uint16_t* out;         // [rows][Hq*hd]: packed-B when out_packed else row-major
   int out_packed;

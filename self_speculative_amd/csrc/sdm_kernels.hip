@@ -881,6 +881,13 @@ hipError_t launch_gemm_w4(int epi, const uint8_t* W, const uint16_t* X, int64_t 
 //                      while the current one is computed (long contexts with
 //                      at most four query tiles, no candidate slots).
 // ---------------------------------------------------------------------------
+// A split's partial O, per (slot, KV head, split): [head_dim / 4][column]
+// float4s, so that a wave's lanes (consecutive columns) write and read four
+// consecutive dims each in one coalesced 16-byte access.
+__device__ __forceinline__ float4* attn_opart4(const AttnArgs& a, int64_t base_idx, int d4, int c) {
+  return (float4*)a.opart + (base_idx * (kHd / 4) + d4) * a.nq_pad + c;
+}
+
 struct AttnState {
   float m, l;
   f32x16 o[4];  // O^T: dims dt * 32 + crow(r, h), this lane's query column
@@ -1035,7 +1042,10 @@ __device__ __forceinline__ const uint16_t* attn_keys_base(const AttnArgs& a, con
 template <bool QLO, bool QPACK>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   __shared__ float s_ml[4][2][32];
-  __shared__ float s_o[4][kHd][32];
+  // page states' O, [wave][column][dims / 4], padded to 33 float4 a column
+  // so that the merge's 16-byte reads of consecutive columns spread over
+  // the banks
+  __shared__ float4 s_o[4][32][kHd / 4 + 1];
   const int slot = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int seq = a.slots.ids[slot];
@@ -1078,13 +1088,16 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     s_ml[wave][0][lane & 31] = st.m;
     s_ml[wave][1][lane & 31] = st.l;
   }
+  // registers 4i..4i+3 of dims tile dt hold dims dt * 32 + 8i + 4h + 0..3
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_o[wave][dt * 32 + crow(r, h)][lane & 31] = st.o[dt][r];
+    for (int i = 0; i < 4; ++i)
+      s_o[wave][lane & 31][dt * 8 + 2 * i + h] =
+          make_float4(st.o[dt][4 * i], st.o[dt][4 * i + 1], st.o[dt][4 * i + 2], st.o[dt][4 * i + 3]);
   __syncthreads();
   const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
-  const int col = threadIdx.x & 31;
+  const int col = threadIdx.x & 31, dg = threadIdx.x >> 5;  // this thread merges dims 16 dg .. 16 dg + 15
   const int cc = qt * 32 + col;
   if (cc < nq) {
     float ca[4], cb[4];
@@ -1096,12 +1109,18 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       Lsum = ca[w] * Lsum + cb[w] * s_ml[w][1][col];
       M = Mn;
     }
-    float* op = a.opart + base_idx * kHd * a.nq_pad;
-    for (int d = threadIdx.x >> 5; d < kHd; d += 8) {
-      float v = s_o[0][d][col];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) v = ca[w] * v + cb[w] * s_o[w][d][col];
-      op[(int64_t)d * a.nq_pad + cc] = v;
+    for (int j = 0; j < 4; ++j) {
+      float4 v = s_o[0][col][4 * dg + j];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 u = s_o[w][col][4 * dg + j];
+        v.x = ca[w] * v.x + cb[w] * u.x;
+        v.y = ca[w] * v.y + cb[w] * u.y;
+        v.z = ca[w] * v.z + cb[w] * u.z;
+        v.w = ca[w] * v.w + cb[w] * u.w;
+      }
+      *attn_opart4(a, base_idx, 4 * dg + j, cc) = v;
     }
     if (threadIdx.x < 32) {
       a.mlpart[(base_idx * 2 + 0) * a.nq_pad + cc] = M;
@@ -1186,11 +1205,12 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
     }
     const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
     if (cval) {
-      float* op = a.opart + base_idx * kHd * a.nq_pad + c;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) op[(int64_t)(dt * 32 + crow(r, h)) * a.nq_pad] = run.o[dt][r];
+        for (int i = 0; i < 4; ++i)
+          *attn_opart4(a, base_idx, dt * 8 + 2 * i + h, c) =
+              make_float4(run.o[dt][4 * i], run.o[dt][4 * i + 1], run.o[dt][4 * i + 2], run.o[dt][4 * i + 3]);
       if (h == 0) {
         a.mlpart[(base_idx * 2 + 0) * a.nq_pad + c] = run.m;
         a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = run.l;
@@ -1291,11 +1311,12 @@ __global__ __launch_bounds__(256) void k_attn_stream_bf16(AttnArgs a, int ns) {
         }
         if (w == 3 && cval) {
           const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp0 + sp;
-          float* op = a.opart + base_idx * kHd * a.nq_pad + c;
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) op[(int64_t)(dt * 32 + crow(r, h)) * a.nq_pad] = run.o[dt][r];
+            for (int i = 0; i < 4; ++i)
+              *attn_opart4(a, base_idx, dt * 8 + 2 * i + h, c) =
+                  make_float4(run.o[dt][4 * i], run.o[dt][4 * i + 1], run.o[dt][4 * i + 2], run.o[dt][4 * i + 3]);
           if (h == 0) {
             a.mlpart[(base_idx * 2 + 0) * a.nq_pad + c] = run.m;
             a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = run.l;
@@ -1311,35 +1332,56 @@ __global__ __launch_bounds__(256) void k_attn_stream_bf16(AttnArgs a, int ns) {
 // Merge the splits for 32 query columns x 16 dims of one (slot, KV head):
 // o = sum_s w_s O_s / sum_s w_s l_s with w_s = exp(m_s - max_s m_s), split
 // order fixed; written as bf16 (hi, plus the lo plane when out_plane is set).
-// The splits' (m, l) go to LDS with all 256 threads loading, the weights are
-// formed there, then every thread sums two (dim, column) outputs with its
-// partial-O loads issued 8 splits at a time.
-__global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
+// Thread (column, group) sums 4 consecutive dims of its column, reading each
+// split's partial with one 16-byte load (coalesced over the columns) and
+// writing each output plane with one 8-byte store.  The splits' (m, l) go
+// to LDS, loaded in one batch per thread, and the weights are formed there;
+// the partials of the first kPre splits are requested before that pass so
+// that both round trips overlap.
+constexpr int kCombineThreads = 128;  // 32 columns x 4 groups of 4 dims
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine_bf16(AttnArgs a) {
   __shared__ float s_m[kMaxSplits][32];
   __shared__ float s_l[kMaxSplits][32];
   __shared__ float s_inv[32];
+  constexpr int NG = kCombineThreads / 32;  // groups of 4 dims
   const int ct = blockIdx.x, dch = blockIdx.y % (kHd / 16), g = blockIdx.y / (kHd / 16), slot = blockIdx.z;
   const int T = a.slots.T;
   const int Hkv = a.kv.Hkv, G = a.Hq / Hkv, nq = G * T;
   const int nsp = attn_splits(a.slots, slot);
   const int64_t b0 = ((int64_t)slot * Hkv + g) * a.max_splits;
-  const int col = threadIdx.x & 31, row = threadIdx.x >> 5;
+  const int col = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int c = ct * 32 + col;
   const bool cval = c < nq;
-  // this thread's partial outputs of the first kPre splits are requested
-  // before the (m, l) pass so that both round trips overlap
+  const int d0 = dch * 16 + 4 * grp;  // this thread's dims d0 .. d0 + 3
   constexpr int kPre = 16;
-  const int64_t sstride = (int64_t)kHd * a.nq_pad;
-  float pre[2][kPre];
+  const int64_t sstride = (int64_t)a.nq_pad * kHd / 4;  // float4s from one split's partial to the next
+  const float4* op = cval ? attn_opart4(a, b0, d0 / 4, c) : nullptr;
+  float4 pre[kPre];
   if (cval) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float* op = a.opart + (b0 * kHd + dch * 16 + row + 8 * j) * a.nq_pad + c;
+    for (int i = 0; i < kPre; ++i)
+      if (i < nsp) pre[i] = op[i * sstride];
+  }
+  // (m, l) of splits grp, grp + NG, ...: the first kML of them in one batch
+  constexpr int kML = 32 / NG;
+  float pm[kML], pl[kML];
 #pragma unroll
-      for (int i = 0; i < kPre; ++i) pre[j][i] = i < nsp ? op[i * sstride] : 0.f;
+  for (int i = 0; i < kML; ++i) {
+    const int s = grp + NG * i;
+    if (s < nsp && cval) {
+      pm[i] = a.mlpart[((b0 + s) * 2) * a.nq_pad + c];
+      pl[i] = a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c];
     }
   }
-  for (int s = row; s < nsp; s += 8) {
+#pragma unroll
+  for (int i = 0; i < kML; ++i) {
+    const int s = grp + NG * i;
+    if (s < nsp) {
+      s_m[s][col] = cval ? pm[i] : -INFINITY;
+      s_l[s][col] = cval ? pl[i] : 0.f;
+    }
+  }
+  for (int s = grp + NG * kML; s < nsp; s += NG) {
     s_m[s][col] = cval ? a.mlpart[((b0 + s) * 2) * a.nq_pad + c] : -INFINITY;
     s_l[s][col] = cval ? a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c] : 0.f;
   }
@@ -1362,30 +1404,38 @@ __global__ __launch_bounds__(256) void k_attn_combine_bf16(AttnArgs a) {
   const int64_t m = (int64_t)slot * T + t;
   const int64_t K = (int64_t)a.Hq * kHd;
   const float inv = s_inv[col];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float w, const float4& q) {
+    acc.x += w * q.x;
+    acc.y += w * q.y;
+    acc.z += w * q.z;
+    acc.w += w * q.w;
+  };
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int d = dch * 16 + row + 8 * j;
-    const float* op = a.opart + (b0 * kHd + d) * a.nq_pad + c;
-    float acc = 0.f;
+  for (int i = 0; i < kPre; ++i)
+    if (i < nsp) add(s_m[i][col], pre[i]);
+  int s = kPre;
+  for (; s + 4 <= nsp; s += 4) {
+    float4 v[4];
 #pragma unroll
-    for (int i = 0; i < kPre; ++i)
-      if (i < nsp) acc += s_m[i][col] * pre[j][i];
-    int s = kPre;
-    for (; s + 8 <= nsp; s += 8) {
-      float v[8];
+    for (int i = 0; i < 4; ++i) v[i] = op[(s + i) * sstride];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = op[(int64_t)(s + i) * sstride];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc += s_m[s + i][col] * v[i];
-    }
-    for (; s < nsp; ++s) acc += s_m[s][col] * op[(int64_t)s * sstride];
-    const float o = acc * inv;
-    const int64_t k = (int64_t)(g * G + hl) * kHd + d;
-    const int64_t oi = a.out_packed ? packed_index(m, k, K) : m * K + k;
-    const uint16_t ob = f2bf(o);
-    a.out[oi] = ob;
-    if (a.out_plane) a.out[a.out_plane + oi] = f2bf_lo(o, ob);
+    for (int i = 0; i < 4; ++i) add(s_m[s + i][col], v[i]);
   }
+  for (; s < nsp; ++s) add(s_m[s][col], op[s * sstride]);
+  // 4 consecutive features of row m: one run in either output layout
+  const int64_t k = (int64_t)(g * G + hl) * kHd + d0;
+  const int64_t oi = a.out_packed ? packed_index(m, k, K) : m * K + k;
+  const float o[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  uint32_t oh[2], ol[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint16_t h0 = f2bf(o[2 * e]), h1 = f2bf(o[2 * e + 1]);
+    oh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    ol[e] = (uint32_t)f2bf_lo(o[2 * e], h0) | ((uint32_t)f2bf_lo(o[2 * e + 1], h1) << 16);
+  }
+  *(uint2*)(a.out + oi) = make_uint2(oh[0], oh[1]);
+  if (a.out_plane) *(uint2*)(a.out + a.out_plane + oi) = make_uint2(ol[0], ol[1]);
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st) {
@@ -1420,8 +1470,8 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   return hipGetLastError();
 }
 hipError_t launch_attn_combine_bf16(const AttnArgs& a, hipStream_t st) {
-  SDM_LAUNCH(k_attn_combine_bf16, dim3(a.nq_pad / 32, a.kv.Hkv * (kHd / 16), a.slots.n_seq), dim3(256), 0, st,
-                     a);
+  SDM_LAUNCH(k_attn_combine_bf16, dim3(a.nq_pad / 32, a.kv.Hkv * (kHd / 16), a.slots.n_seq), dim3(kCombineThreads), 0, st,
+             a);
   return hipGetLastError();
 }
 
