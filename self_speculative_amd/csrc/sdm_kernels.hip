@@ -389,16 +389,29 @@ __device__ __forceinline__ void gemm_epilogue(const float (&c)[16], int nt, int 
     for (int j = 0; j < 4; ++j) *(float4*)(pr + 8 * j) = make_float4(c[4 * j], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]);
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (!valid) return;
+    // registers 4i..4i+3 are features 16 nt + 8i + 4h + 0..3, contiguous in
+    // the packed layout: one 8-byte store per plane and group
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int f = 16 * nt + crow(r, h);
-      const float g = c[r], u = c[r + 8];
-      const float s = g / (1.f + expf(-g));
-      const float y = s * u;
-      const uint16_t hb = f2bf(y);
-      const int64_t pi = packed_index(m, f, ea.F);
-      ea.h_out[pi] = hb;
-      ea.h_out[ea.h_plane + pi] = f2bf_lo(y, hb);
+    for (int i = 0; i < 2; ++i) {
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * i + e;
+        const float g = c[r], u = c[r + 8];
+        const float s = g / (1.f + expf(-g));
+        const float y = s * u;
+        const uint16_t hb = f2bf(y), lb = f2bf_lo(y, hb);
+        if (e & 1) {
+          hw[e >> 1] |= (uint32_t)hb << 16;
+          lw[e >> 1] |= (uint32_t)lb << 16;
+        } else {
+          hw[e >> 1] = hb;
+          lw[e >> 1] = lb;
+        }
+      }
+      const int64_t pi = packed_index(m, 16 * nt + crow(4 * i, h), ea.F);
+      *(uint2*)(ea.h_out + pi) = make_uint2(hw[0], hw[1]);
+      *(uint2*)(ea.h_out + ea.h_plane + pi) = make_uint2(lw[0], lw[1]);
     }
   } else {  // EPI_LOGITS
     Rec a = rec_empty();
@@ -541,21 +554,35 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   for (int b = nch * kGemmChunk + wave; b < kbs; b += WAVES) one_block(kbase + b);
 
   if constexpr (MT == 1) {
-    // all TP tiles through LDS at once; wave t sums tile t over the waves in order
-    __shared__ float red[TP][WAVES][16][64];
+    // all TP tiles through LDS at once, a lane's 16 values as four 16-byte
+    // words, word i at slot i ^ sw (lanes 4j..4j+3 of each 16 then hit
+    // different banks); wave t sums tile t over the waves in order
+    __shared__ float4 red[TP][WAVES][64][4];
+    const int sw = (lane >> 2) & 3;
 #pragma unroll
     for (int t = 0; t < TP; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[t][wave][r][lane] = acc[0][t][r];
+      for (int i = 0; i < 4; ++i)
+        red[t][wave][lane][i ^ sw] = make_float4(acc[0][t][4 * i], acc[0][t][4 * i + 1], acc[0][t][4 * i + 2],
+                                                 acc[0][t][4 * i + 3]);
     __syncthreads();
     if (wave < TP) {
       float c[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = red[wave][0][r][lane];
+      for (int i = 0; i < 4; ++i) {
+        float4 v = red[wave][0][lane][i ^ sw];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
-        c[r] = v;
+        for (int w = 1; w < WAVES; ++w) {
+          const float4 u = red[wave][w][lane][i ^ sw];
+          v.x += u.x;
+          v.y += u.y;
+          v.z += u.z;
+          v.w += u.w;
+        }
+        c[4 * i] = v.x;
+        c[4 * i + 1] = v.y;
+        c[4 * i + 2] = v.z;
+        c[4 * i + 3] = v.w;
       }
       gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, sk, lane, ea, pre);
     }
