@@ -1063,11 +1063,12 @@ __device__ __forceinline__ const uint16_t* attn_keys_base(const AttnArgs& a, con
   return attn_page_base(a, seq, jw);
 }
 
-// Grid: linear id -> (pair = split * Hkv + g, query tile); workgroups sharing
-// a pair get linear ids congruent mod 8 so that they are placed on the same
-// XCD and share its L2 for the K/V pages.
+// Grid: linear id -> (pair = split * Hkv + g, query tile qt0 + j); workgroups
+// sharing a pair get linear ids congruent mod 8 so that they are placed on
+// the same XCD and share its L2 for the K/V pages.  qt0 > 0 when the staged
+// shape runs the first qt0 tiles.
 template <bool QLO, bool QPACK>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, int qt0) {
   __shared__ float s_ml[4][2][32];
   // page states' O, [wave][column][dims / 4], padded to 33 float4 a column
   // so that the merge's 16-byte reads of consecutive columns spread over
@@ -1084,8 +1085,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int nqt = (nq + 31) >> 5;
   const int nsp = attn_splits(a.slots, slot);
   const int L = blockIdx.x;
-  const int qt = (L % (8 * nqt)) / 8;
-  const int pair = (L / (8 * nqt)) * 8 + (L % 8);
+  const int nsub = nqt - qt0;  // the query tiles of this launch
+  const int qt = qt0 + (L % (8 * nsub)) / 8;
+  const int pair = (L / (8 * nsub)) * 8 + (L % 8);
   if (pair >= nsp * Hkv) return;
   const int sp = pair / Hkv, g = pair % Hkv;
   const AttnKeys ks = attn_keys(a, slot, n, T, sp, nsp);
@@ -1157,7 +1159,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
 }
 
 template <bool QLO, bool QPACK>
-__global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a, int exact) {
   __shared__ u32x4 s_k[4][16][64];  // the split's four pages: K operand tiles
   __shared__ u32x4 s_v[4][16][64];  //                        and V^T operand tiles
   const int slot = blockIdx.y;
@@ -1172,8 +1174,10 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
   const int nsp = attn_splits(a.slots, slot);
   // linear id -> (pair = split * Hkv + g, group of query tiles); the groups
   // of a pair get ids congruent mod 8, so they share an XCD's L2.  Groups
-  // hold four tiles; the last one also takes the remainder (up to seven)
-  const int nqg = nqt >= 8 ? nqt >> 2 : 1;
+  // hold four tiles.  With exact, the nqt % 4 tiles past the last whole
+  // group are left to a tile-parallel launch; else the last group also
+  // takes them (up to seven tiles)
+  const int nqg = exact || nqt >= 8 ? nqt >> 2 : 1;
   const int L = blockIdx.x;
   const int qg = (L % (8 * nqg)) / 8;
   const int pair = (L / (8 * nqg)) * 8 + (L % 8);
@@ -1198,7 +1202,7 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a) {
     }
   }
   __syncthreads();
-  const int qt_end = qg == nqg - 1 ? nqt : 4 * qg + 4;
+  const int qt_end = qg == nqg - 1 && !exact ? nqt : 4 * qg + 4;
   for (int qt = 4 * qg + wave; qt < qt_end; qt += 4) {
     const int c = qt * 32 + (lane & 31);
     const bool cval = c < nq;
@@ -1465,6 +1469,14 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine_bf16(AttnArgs 
   if (a.out_plane) *(uint2*)(a.out + a.out_plane + oi) = make_uint2(ol[0], ol[1]);
 }
 
+// A launch with explicit timing events, either of which may be null.
+template <typename... KArgs, typename... Args>
+static void launch_with_events(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t e0,
+                               hipEvent_t e1, Args... args) {
+  if (e0 || e1) hipExtLaunchKernelGGL(kern, grid, block, 0, st, e0, e1, 0, args...);
+  else hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
+}
+
 hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t st) {
   const int nqt = (a.Hq / a.kv.Hkv * a.slots.T + 31) / 32;
   const int pairs = grid_splits * a.kv.Hkv;
@@ -1484,15 +1496,29 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   // per query tile)
   const int nqg = nqt >= 8 ? nqt / 4 : 1;
   const bool staged = (int64_t)pairs * nqg * a.slots.n_seq >= kAttnStagedPairs;
-  const dim3 grd(staged ? (pairs + 7) / 8 * 8 * nqg : (pairs + 7) / 8 * 8 * nqt, a.slots.n_seq), blk(256);
-  if (a.q_plane && a.q_packed) {
-    if (staged) SDM_LAUNCH((k_attn_staged_bf16<true, true>), grd, blk, 0, st, a);
-    else SDM_LAUNCH((k_attn_bf16<true, true>), grd, blk, 0, st, a);
-  } else if (!a.q_plane && !a.q_packed) {
-    if (staged) SDM_LAUNCH((k_attn_staged_bf16<false, false>), grd, blk, 0, st, a);
-    else SDM_LAUNCH((k_attn_bf16<false, false>), grd, blk, 0, st, a);
-  } else {
+  // a remainder of nqt % 4 tiles would make one wave of a group run two
+  // tiles while the other three wait: the staged launch then takes whole
+  // groups of four and a tile-parallel launch the remainder
+  const bool exact = staged && nqt >= 4 && nqt % 4 != 0;
+  const int qt0 = exact ? nqt / 4 * 4 : 0;
+  const int64_t pairs8 = (pairs + 7) / 8 * 8;
+  const dim3 blk(256);
+  const dim3 grd_staged(pairs8 * (exact ? nqt / 4 : nqg), a.slots.n_seq), grd_tile(pairs8 * (nqt - qt0), a.slots.n_seq);
+  if (!(a.q_plane && a.q_packed) && !(!a.q_plane && !a.q_packed))
     return hipErrorInvalidValue;  // hi/lo queries come packed, plain ones row-major
+  // a timed call's events go on its first dispatch's start and its last
+  // dispatch's completion
+  const KernelTiming kt = g_ktiming;
+  g_ktiming = KernelTiming{};
+  if (staged) {
+    const hipEvent_t e1 = exact ? nullptr : kt.stop;
+    if (a.q_plane) launch_with_events(k_attn_staged_bf16<true, true>, grd_staged, blk, st, kt.start, e1, a, (int)exact);
+    else launch_with_events(k_attn_staged_bf16<false, false>, grd_staged, blk, st, kt.start, e1, a, (int)exact);
+  }
+  if (!staged || exact) {
+    const hipEvent_t e0 = staged ? nullptr : kt.start;
+    if (a.q_plane) launch_with_events(k_attn_bf16<true, true>, grd_tile, blk, st, e0, kt.stop, a, qt0);
+    else launch_with_events(k_attn_bf16<false, false>, grd_tile, blk, st, e0, kt.stop, a, qt0);
   }
   return hipGetLastError();
 }

@@ -98,3 +98,20 @@ def test_attention_op_row_independence():
     for i in (0, 5, 31):
         one = run_gpu(q[i:i + 1], k[: P + i + 1], v[: P + i + 1], P + i, 1, O.CAUSAL)
         np.testing.assert_array_equal(one[0], ca[i])
+
+
+def test_attention_op_staged_with_remainder_tile():
+    """40 q / 8 KV heads (five query tiles per KV head) over a prefix long
+    enough for the staged shape: whole groups of four tiles are staged and
+    the fifth tile runs tile-parallel, in two launches.  Parity with the
+    oracle, and the remainder tile's rows bit-equal to the same rows
+    computed as one-row blocks (where all five heads share one staged tile)."""
+    P = 8300
+    print(f"attention op heads 40/8, P={P} (staged + remainder tile)", flush=True)
+    q, k, v = W.attention_op_inputs(P, 32, 40, 8, HD, seed=5)
+    ca = run_gpu(q, k, v, P, 32, O.CAUSAL, hq=40, hkv=8)
+    check_close(ca, oracle_attn(q, k, v, P, O.CAUSAL))
+    check_close(run_gpu(q, k, v, P, 32, O.BIDIR, hq=40, hkv=8), oracle_attn(q, k, v, P, O.BIDIR))
+    for i in (0, 17, 31):
+        one = run_gpu(q[i:i + 1], k[: P + i + 1], v[: P + i + 1], P + i, 1, O.CAUSAL, hq=40, hkv=8)
+        np.testing.assert_array_equal(one[0], ca[i])
