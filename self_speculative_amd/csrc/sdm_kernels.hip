@@ -1412,21 +1412,48 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine_bf16(AttnArgs 
       s_l[s][col] = cval ? pl[i] : 0.f;
     }
   }
-  for (int s = grp + NG * kML; s < nsp; s += NG) {
-    s_m[s][col] = cval ? a.mlpart[((b0 + s) * 2) * a.nq_pad + c] : -INFINITY;
-    s_l[s][col] = cval ? a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c] : 0.f;
+  // further splits (long contexts) in batches of kML, each batch's loads
+  // issued together
+  for (int s0 = grp + NG * kML; s0 < nsp; s0 += NG * kML) {
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+      const int s = s0 + NG * i;
+      if (s < nsp && cval) {
+        pm[i] = a.mlpart[((b0 + s) * 2) * a.nq_pad + c];
+        pl[i] = a.mlpart[((b0 + s) * 2 + 1) * a.nq_pad + c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+      const int s = s0 + NG * i;
+      if (s < nsp) {
+        s_m[s][col] = cval ? pm[i] : -INFINITY;
+        s_l[s][col] = cval ? pl[i] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // the largest max (each group scans splits grp, grp + NG, ...; a max is
+  // exact in any order), then every split's weight, both by all threads
+  __shared__ float s_gmax[NG][32];
+  {
+    float mx = -INFINITY;
+    for (int s = grp; s < nsp; s += NG) mx = fmaxf(mx, s_m[s][col]);
+    s_gmax[grp][col] = mx;
+  }
+  __syncthreads();
+  float M = s_gmax[0][col];
+#pragma unroll
+  for (int i = 1; i < NG; ++i) M = fmaxf(M, s_gmax[i][col]);
+  for (int s = grp; s < nsp; s += NG) {
+    const float ms = s_m[s][col];
+    s_m[s][col] = (ms == -INFINITY) ? 0.f : __expf(ms - M);  // weight replaces the max
   }
   __syncthreads();
   if (threadIdx.x < 32) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, s_m[s][col]);
-    float L = 0.f;
-    for (int s = 0; s < nsp; ++s) {
-      const float ms = s_m[s][col];
-      const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-      s_m[s][col] = w;  // weight replaces the max
-      L += w * s_l[s][col];
-    }
+    float L = 0.f;  // in split order
+#pragma unroll 8
+    for (int s = 0; s < nsp; ++s) L += s_m[s][col] * s_l[s][col];
     s_inv[col] = 1.f / L;
   }
   __syncthreads();
@@ -1445,7 +1472,15 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine_bf16(AttnArgs 
 #pragma unroll
   for (int i = 0; i < kPre; ++i)
     if (i < nsp) add(s_m[i][col], pre[i]);
+  // further splits in batches of 16 loads in flight
   int s = kPre;
+  for (; s + 16 <= nsp; s += 16) {
+    float4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = op[(s + i) * sstride];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) add(s_m[s + i][col], v[i]);
+  }
   for (; s + 4 <= nsp; s += 4) {
     float4 v[4];
 #pragma unroll
