@@ -826,23 +826,38 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
   // The MT x TP output tiles (activation tile major, at most 4) go through
   // LDS; wave q sums tile q over the waves in order (after undoing
   // w4_operand's factor 16, exactly) and finishes it.
-  __shared__ float red[4][WAVES][16][64];
+  // a lane's 16 values as four 16-byte words, word i at slot i ^ sw (lanes
+  // 4j..4j+3 of each 16 then hit different banks)
+  __shared__ float4 red[4][WAVES][64][4];
   const int ntile = mcount * TP;
+  const int sw = (lane >> 2) & 3;
 #pragma unroll
   for (int q = 0; q < MT * TP; ++q)
     if (q < ntile) {
+      const f32x16& tq = tot[q / TP][q % TP];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[q][wave][r][lane] = tot[q / TP][q % TP][r] * 0.0625f;
+      for (int i = 0; i < 4; ++i)
+        red[q][wave][lane][i ^ sw] = make_float4(tq[4 * i] * 0.0625f, tq[4 * i + 1] * 0.0625f,
+                                                 tq[4 * i + 2] * 0.0625f, tq[4 * i + 3] * 0.0625f);
     }
   __syncthreads();
   if (wave < ntile) {
     float c[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = red[wave][0][r][lane];
+    for (int i = 0; i < 4; ++i) {
+      float4 v = red[wave][0][lane][i ^ sw];
 #pragma unroll
-      for (int w = 1; w < WAVES; ++w) v += red[wave][w][r][lane];
-      c[r] = v;
+      for (int w = 1; w < WAVES; ++w) {
+        const float4 u = red[wave][w][lane][i ^ sw];
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+      c[4 * i] = v.x;
+      c[4 * i + 1] = v.y;
+      c[4 * i + 2] = v.z;
+      c[4 * i + 3] = v.w;
     }
     if constexpr (MT == 1) gemm_epilogue<EPI, true>(c, nt0 + wave, mt0, sk, lane, ea, pre);
     else gemm_epilogue<EPI, false>(c, nt0 + wave % TP, mt0 + wave / TP, sk, lane, ea, pre);
