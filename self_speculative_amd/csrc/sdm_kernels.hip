@@ -1078,17 +1078,70 @@ __device__ __forceinline__ const uint16_t* attn_keys_base(const AttnArgs& a, con
   return attn_page_base(a, seq, jw);
 }
 
+// The four page states of one query tile (waves 0..3 hold pages 0..3 of a
+// split) meet in LDS; attn_merge_store merges them per column in page order,
+// pairwise, and writes the split's partial (all 256 threads; thread (col, dg)
+// takes dims 16 dg .. 16 dg + 15 of column col).
+struct AttnMergeLds {
+  float ml[4][2][32];
+  // O as [wave][column][dims / 4], padded to 33 float4 a column so that the
+  // merge's 16-byte reads of consecutive columns spread over the banks
+  float4 o[4][32][kHd / 4 + 1];
+};
+__device__ __forceinline__ void attn_merge_put(AttnMergeLds& sm, const AttnState& st, int wave, int lane) {
+  const int h = lane >> 5;
+  if (h == 0) {
+    sm.ml[wave][0][lane & 31] = st.m;
+    sm.ml[wave][1][lane & 31] = st.l;
+  }
+  // registers 4i..4i+3 of dims tile dt hold dims dt * 32 + 8i + 4h + 0..3
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sm.o[wave][lane & 31][dt * 8 + 2 * i + h] =
+          make_float4(st.o[dt][4 * i], st.o[dt][4 * i + 1], st.o[dt][4 * i + 2], st.o[dt][4 * i + 3]);
+}
+__device__ __forceinline__ void attn_merge_store(const AttnArgs& a, const AttnMergeLds& sm, int64_t base_idx, int qt,
+                                                 int nq) {
+  const int col = threadIdx.x & 31, dg = threadIdx.x >> 5;
+  const int cc = qt * 32 + col;
+  if (cc >= nq) return;
+  float ca[4], cb[4];
+  float M = sm.ml[0][0][col], Lsum = sm.ml[0][1][col];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    float Mn;
+    attn_merge_coef(M, sm.ml[w][0][col], Mn, ca[w], cb[w]);
+    Lsum = ca[w] * Lsum + cb[w] * sm.ml[w][1][col];
+    M = Mn;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float4 v = sm.o[0][col][4 * dg + j];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 u = sm.o[w][col][4 * dg + j];
+      v.x = ca[w] * v.x + cb[w] * u.x;
+      v.y = ca[w] * v.y + cb[w] * u.y;
+      v.z = ca[w] * v.z + cb[w] * u.z;
+      v.w = ca[w] * v.w + cb[w] * u.w;
+    }
+    *attn_opart4(a, base_idx, 4 * dg + j, cc) = v;
+  }
+  if (threadIdx.x < 32) {
+    a.mlpart[(base_idx * 2 + 0) * a.nq_pad + cc] = M;
+    a.mlpart[(base_idx * 2 + 1) * a.nq_pad + cc] = Lsum;
+  }
+}
+
 // Grid: linear id -> (pair = split * Hkv + g, query tile qt0 + j); workgroups
 // sharing a pair get linear ids congruent mod 8 so that they are placed on
 // the same XCD and share its L2 for the K/V pages.  qt0 > 0 when the staged
 // shape runs the first qt0 tiles.
 template <bool QLO, bool QPACK>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, int qt0) {
-  __shared__ float s_ml[4][2][32];
-  // page states' O, [wave][column][dims / 4], padded to 33 float4 a column
-  // so that the merge's 16-byte reads of consecutive columns spread over
-  // the banks
-  __shared__ float4 s_o[4][32][kHd / 4 + 1];
+  __shared__ AttnMergeLds sm;
   const int slot = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int seq = a.slots.ids[slot];
@@ -1128,55 +1181,22 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a, int qt0) {
   attn_page_state<QLO>(a, [&](int i) { return kv_k[i]; }, [&](int i) { return kv_v[i]; }, qop, qlo, jw, ks.jend,
                        ks.jall, n + t, cval, h, st);
   // the page states meet in LDS; per column, merged in page order
-  if (h == 0) {
-    s_ml[wave][0][lane & 31] = st.m;
-    s_ml[wave][1][lane & 31] = st.l;
-  }
-  // registers 4i..4i+3 of dims tile dt hold dims dt * 32 + 8i + 4h + 0..3
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s_o[wave][lane & 31][dt * 8 + 2 * i + h] =
-          make_float4(st.o[dt][4 * i], st.o[dt][4 * i + 1], st.o[dt][4 * i + 2], st.o[dt][4 * i + 3]);
+  attn_merge_put(sm, st, wave, lane);
   __syncthreads();
-  const int64_t base_idx = ((int64_t)slot * Hkv + g) * a.max_splits + sp;
-  const int col = threadIdx.x & 31, dg = threadIdx.x >> 5;  // this thread merges dims 16 dg .. 16 dg + 15
-  const int cc = qt * 32 + col;
-  if (cc < nq) {
-    float ca[4], cb[4];
-    float M = s_ml[0][0][col], Lsum = s_ml[0][1][col];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      float Mn;
-      attn_merge_coef(M, s_ml[w][0][col], Mn, ca[w], cb[w]);
-      Lsum = ca[w] * Lsum + cb[w] * s_ml[w][1][col];
-      M = Mn;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float4 v = s_o[0][col][4 * dg + j];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        const float4 u = s_o[w][col][4 * dg + j];
-        v.x = ca[w] * v.x + cb[w] * u.x;
-        v.y = ca[w] * v.y + cb[w] * u.y;
-        v.z = ca[w] * v.z + cb[w] * u.z;
-        v.w = ca[w] * v.w + cb[w] * u.w;
-      }
-      *attn_opart4(a, base_idx, 4 * dg + j, cc) = v;
-    }
-    if (threadIdx.x < 32) {
-      a.mlpart[(base_idx * 2 + 0) * a.nq_pad + cc] = M;
-      a.mlpart[(base_idx * 2 + 1) * a.nq_pad + cc] = Lsum;
-    }
-  }
+  attn_merge_store(a, sm, ((int64_t)slot * Hkv + g) * a.max_splits + sp, qt, nq);
 }
 
+constexpr int kStagedLastGroup = 0, kStagedExact = 1, kStagedFold = 2;
+
 template <bool QLO, bool QPACK>
-__global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a, int exact) {
-  __shared__ u32x4 s_k[4][16][64];  // the split's four pages: K operand tiles
-  __shared__ u32x4 s_v[4][16][64];  //                        and V^T operand tiles
+__global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a, int rem) {
+  // the split's four pages (K operand tiles, then V^T operand tiles); with
+  // rem == kStagedFold the same memory then holds the remainder tile's four
+  // page states for their merge
+  __shared__ u32x4 s_pages[2][4][16][64];
+  u32x4 (&s_k)[4][16][64] = s_pages[0];
+  u32x4 (&s_v)[4][16][64] = s_pages[1];
+  static_assert(sizeof(AttnMergeLds) <= sizeof(s_pages), "the merge fits in the page buffers");
   const int slot = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int seq = a.slots.ids[slot];
@@ -1189,10 +1209,13 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a, int exact)
   const int nsp = attn_splits(a.slots, slot);
   // linear id -> (pair = split * Hkv + g, group of query tiles); the groups
   // of a pair get ids congruent mod 8, so they share an XCD's L2.  Groups
-  // hold four tiles.  With exact, the nqt % 4 tiles past the last whole
-  // group are left to a tile-parallel launch; else the last group also
-  // takes them (up to seven tiles)
-  const int nqg = exact || nqt >= 8 ? nqt >> 2 : 1;
+  // hold four tiles.  The nqt % 4 tiles past the last whole group:
+  //   kStagedLastGroup  the last group runs them too (up to seven tiles);
+  //   kStagedExact      a tile-parallel launch runs them;
+  //   kStagedFold       one tile: the last group's wave w forms its page w
+  //                     state, and the four meet in LDS as in the
+  //                     tile-parallel shape
+  const int nqg = rem != kStagedLastGroup || nqt >= 8 ? nqt >> 2 : 1;
   const int L = blockIdx.x;
   const int qg = (L % (8 * nqg)) / 8;
   const int pair = (L / (8 * nqg)) * 8 + (L % 8);
@@ -1217,7 +1240,7 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a, int exact)
     }
   }
   __syncthreads();
-  const int qt_end = qg == nqg - 1 && !exact ? nqt : 4 * qg + 4;
+  const int qt_end = qg == nqg - 1 && rem == kStagedLastGroup ? nqt : 4 * qg + 4;
   for (int qt = 4 * qg + wave; qt < qt_end; qt += 4) {
     const int c = qt * 32 + (lane & 31);
     const bool cval = c < nq;
@@ -1262,6 +1285,28 @@ __global__ __launch_bounds__(256) void k_attn_staged_bf16(AttnArgs a, int exact)
         a.mlpart[(base_idx * 2 + 1) * a.nq_pad + c] = run.l;
       }
     }
+  }
+  if (rem == kStagedFold && qg == nqg - 1) {
+    // the remainder tile, page by page: wave w forms page w's state
+    const int qt = nqt - 1;
+    const int c = qt * 32 + (lane & 31);
+    const bool cval = c < nq;
+    const int hl = cval ? c / T : 0, t = cval ? c % T : 0;
+    u32x4 qop[8], qlo[QLO ? 8 : 1];
+    attn_load_q<QLO, QPACK>(a, slot, g, qt, t, g * G + hl, cval, lane, qop, qlo);
+    u32x4 pk[16], pv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pk[i] = s_k[wave][i][lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = s_v[wave][i][lane];
+    AttnState st;
+    attn_page_state<QLO>(a, [&](int i) { return pk[i]; }, [&](int i) { return pv[i]; }, qop, qlo,
+                         ks.split0 + 64 * wave, ks.jend, ks.jall, n + t, cval, h, st);
+    __syncthreads();  // every wave is done with the pages
+    AttnMergeLds& sm = *reinterpret_cast<AttnMergeLds*>(&s_pages[0][0][0][0]);
+    attn_merge_put(sm, st, wave, lane);
+    __syncthreads();
+    attn_merge_store(a, sm, ((int64_t)slot * Hkv + g) * a.max_splits + sp, qt, nq);
   }
 }
 
@@ -1548,12 +1593,17 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   const bool staged = (int64_t)pairs * nqg * a.slots.n_seq >= kAttnStagedPairs;
   // a remainder of nqt % 4 tiles would make one wave of a group run two
   // tiles while the other three wait: the staged launch then takes whole
-  // groups of four and a tile-parallel launch the remainder
-  const bool exact = staged && nqt >= 4 && nqt % 4 != 0;
+  // groups of four, and one remainder tile is folded into the last group
+  // page by page (each wave one page state), more go to a tile-parallel
+  // launch
+  const bool fold = staged && nqt >= 4 && nqt % 4 == 1;
+  const bool exact = staged && nqt >= 4 && nqt % 4 > 1;
+  const int rem = fold ? kStagedFold : exact ? kStagedExact : kStagedLastGroup;
   const int qt0 = exact ? nqt / 4 * 4 : 0;
   const int64_t pairs8 = (pairs + 7) / 8 * 8;
   const dim3 blk(256);
-  const dim3 grd_staged(pairs8 * (exact ? nqt / 4 : nqg), a.slots.n_seq), grd_tile(pairs8 * (nqt - qt0), a.slots.n_seq);
+  const dim3 grd_staged(pairs8 * (exact || fold ? nqt / 4 : nqg), a.slots.n_seq),
+      grd_tile(pairs8 * (nqt - qt0), a.slots.n_seq);
   if (!(a.q_plane && a.q_packed) && !(!a.q_plane && !a.q_packed))
     return hipErrorInvalidValue;  // hi/lo queries come packed, plain ones row-major
   // a timed call's events go on its first dispatch's start and its last
@@ -1562,8 +1612,8 @@ hipError_t launch_attention_bf16(const AttnArgs& a, int grid_splits, hipStream_t
   g_ktiming = KernelTiming{};
   if (staged) {
     const hipEvent_t e1 = exact ? nullptr : kt.stop;
-    if (a.q_plane) launch_with_events(k_attn_staged_bf16<true, true>, grd_staged, blk, st, kt.start, e1, a, (int)exact);
-    else launch_with_events(k_attn_staged_bf16<false, false>, grd_staged, blk, st, kt.start, e1, a, (int)exact);
+    if (a.q_plane) launch_with_events(k_attn_staged_bf16<true, true>, grd_staged, blk, st, kt.start, e1, a, rem);
+    else launch_with_events(k_attn_staged_bf16<false, false>, grd_staged, blk, st, kt.start, e1, a, rem);
   }
   if (!staged || exact) {
     const hipEvent_t e0 = staged ? nullptr : kt.start;
