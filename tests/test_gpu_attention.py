@@ -102,10 +102,11 @@ def test_attention_op_row_independence():
 
 def test_attention_op_staged_with_remainder_tile():
     """40 q / 8 KV heads (five query tiles per KV head) over a prefix long
-    enough for the staged shape: whole groups of four tiles are staged and
-    the fifth tile runs tile-parallel, in two launches.  Parity with the
-    oracle, and the remainder tile's rows bit-equal to the same rows
-    computed as one-row blocks (where all five heads share one staged tile)."""
+    enough for the staged shape: four tiles a group run over the staged
+    pages and the fifth is folded in page by page (each wave one page
+    state, merged in LDS).  Parity with the oracle, and the fifth tile's
+    rows bit-equal to the same rows computed as one-row blocks (where all
+    five heads share one staged tile)."""
     P = 8300
     print(f"attention op heads 40/8, P={P} (staged + remainder tile)", flush=True)
     q, k, v = W.attention_op_inputs(P, 32, 40, 8, HD, seed=5)
