@@ -171,6 +171,24 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   const int mt = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);  // activation tiles per workgroup
   const int mgroups = (g.MTILES + mt - 1) / mt;
   const int tmax = mt == 4 ? 3 : 4;  // register budget: 4 x 4 accumulator tiles do not fit
+  if (mt == 4) {
+    // Many-row launches run one workgroup per compute unit, in rounds of
+    // kGemmTargetGroups, and are bound by operand bytes into the compute
+    // units: 4 activation tiles (two planes) + t weight tiles feed 8t
+    // products, so a group of t tiles costs about (8 + t) / 8 tile-times
+    // per tile.  Take the t that minimises rounds x (8 + t); the last group
+    // may hold fewer tiles.
+    int best = 0;
+    for (int t = tmax; t >= 1; --t) {
+      const int64_t groups = (int64_t)(g.NT + t - 1) / t * g.S * mgroups;
+      const int64_t cost = (groups + kGemmTargetGroups - 1) / kGemmTargetGroups * (8 + t);
+      if (best == 0 || cost < best) {
+        best = (int)cost;
+        g.TP = t;
+      }
+    }
+    return g;
+  }
   for (int t = tmax; t > 1; --t)
     if (g.NT % t == 0 && (g.NT / t) * g.S * mgroups >= kGemmTargetGroups) {
       g.TP = t;

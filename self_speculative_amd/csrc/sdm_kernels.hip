@@ -460,7 +460,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   // activation tiles run a one-dimensional grid placed by many_row_place
   int nt0, sk, mg;
   if constexpr (MT == 4) {
-    const int ntg = g.NT / TP;
+    // the last weight-tile group may hold fewer than TP tiles
+    const int ntg = (g.NT + TP - 1) / TP;
     const ManyRowPlace pl = many_row_place(blockIdx.x, ntg * g.S, (g.MTILES + 3) / 4);
     mg = pl.group;
     nt0 = (pl.unit / g.S) * TP;
@@ -499,6 +500,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
     if (wave < TP) epi_preload<EPI>(pre, nt0 + wave, mt0, lane, ea);
   }
 
+  // tiles of this group: TP, or fewer in a ragged last group of a many-row
+  // launch, whose missing tiles load tile nt0 again and are not finished
+  const int tvalid = MT == 4 ? min(TP, g.NT - nt0) : TP;
+  auto tl = [&](int t) { return MT == 4 && t >= tvalid ? 0 : t; };
   const u32x4* wp = (const u32x4*)W + (int64_t)nt0 * g.KB * 64 + lane;  // tile nt0 + t at t * KB * 64
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
 #pragma unroll
     for (int t = 0; t < TP; ++t)
 #pragma unroll
-      for (int u = 0; u < U; ++u) wv[t][u] = load_weight<MT>(wp + ((int64_t)t * g.KB + kb + boff(u)) * 64);
+      for (int u = 0; u < U; ++u) wv[t][u] = load_weight<MT>(wp + ((int64_t)tl(t) * g.KB + kb + boff(u)) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   auto one_block = [&](int kb) {
     u32x4 wv[TP];
 #pragma unroll
-    for (int t = 0; t < TP; ++t) wv[t] = load_weight<MT>(wp + ((int64_t)t * g.KB + kb) * 64);
+    for (int t = 0; t < TP; ++t) wv[t] = load_weight<MT>(wp + ((int64_t)tl(t) * g.KB + kb) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       if (i < mcount) {
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
         }
       __syncthreads();
       const int q = q0 + wave;
-      if (q < ntile) {
+      if (q < ntile && q % TP < tvalid) {
         float c[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -625,7 +630,8 @@ static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane,
   const int MT = g.MTILES <= 1 ? 1 : (g.MTILES == 2 ? 2 : 4);
   const int TP = g.TP;
   const int mgroups = (g.MTILES + MT - 1) / MT;
-  const dim3 grd = MT == 4 ? dim3(mgroups * (g.NT / TP) * g.S) : dim3(g.NT / TP, g.S, mgroups), blk(64 * WAVES);
+  const dim3 grd = MT == 4 ? dim3(mgroups * ((g.NT + TP - 1) / TP) * g.S) : dim3(g.NT / TP, g.S, mgroups),
+             blk(64 * WAVES);
   // weight loads in flight per wave: 16 tiles at TP 1, 4 * TP otherwise
   constexpr int U1 = WAVES == 8 ? 8 : 16;
   if (MT == 1) {
