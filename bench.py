@@ -164,8 +164,9 @@ def main() -> int:
     log(f"weights drawn in {time.time() - t0:.1f}s")
     prompt = W.prompt_ids(s, args.prompt, seed=0)
     if args.quadratic_only:
-        print(json.dumps({"quadratic": quadratic_bench(log, s, weights, prompt, sched, args.warmup, 4096,
-                                                       n_cyc=args.steps or 40)}), flush=True)
+        q = quadratic_bench(log, s, weights, prompt, sched, args.warmup, 4096, n_cyc=args.steps or 40)
+        torch.cuda.empty_cache()
+        print(json.dumps({"quadratic": q, "vendor_gemm_bf16": vendor_gemm_rate(log)}), flush=True)
         return 0
     K = args.steps if args.steps is not None else 3
     if K < 1:
@@ -446,6 +447,8 @@ def main() -> int:
         torch.cuda.empty_cache()
         out["quadratic"] = quadratic_bench(log, s, weights, prompt, sched, args.warmup, max_ctx,
                                            linear_tpf=cyc_tokens / (2 * gen_cyc))
+        torch.cuda.empty_cache()
+        out["vendor_gemm_bf16"] = vendor_gemm_rate(log)
 
     if args.calib_copy:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
@@ -570,6 +573,31 @@ def gemm_flops(s, cls: str, M: int) -> int:
     nk = {"qkv": (s.qkv_dim, d), "o": (d, s.q_dim), "gate_up": (2 * F, d), "down": (d, F), "lm_head": (s.vocab, d)}
     n, k = nk[cls]
     return 2 * M * n * k
+
+
+def vendor_gemm_rate(log, n: int = 8192, reps: int = 20) -> dict:
+    """A practical reference for the MFMA-bound passes: the vendor library's bf16 GEMM (torch.matmul,
+    hipBLASLt) on an n x n x n product of random N(0, 1) operands, which load the matrix units as real
+    data does (all-zero operands run faster, at lower power)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record(st)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    tflops = 2.0 * n ** 3 / (us * 1e-6) / 1e12
+    del a, b, c
+    log(f"vendor bf16 GEMM {n}^3: {us:.1f} us, {tflops:.1f} TFLOP/s")
+    return {"kernel": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), random N(0,1) operands", "avg_us": round(us, 1),
+            "TFLOPs": round(tflops, 1), "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def quadratic_bench(log, s, weights, prompt, sched, warmup, max_ctx, n_cyc=40, linear_tpf=None) -> dict:
