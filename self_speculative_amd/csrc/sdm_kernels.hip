@@ -777,9 +777,11 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
     if (wave < TP) epi_preload<EPI>(pre, nt0 + wave, mt0, lane, ea);
   }
 
-  const u32x4* wc = (const u32x4*)Wc + lane;   // tile nt, group gr, part p at ((nt * G + gr) * 2 + p) * 64
-  const u32x4* ws = (const u32x4*)Ws + 2 * h;  // tile nt, group gr at (nt * G + gr) * 4
-  const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
+  // uniform bases, indexed with the lane's offset at each load (no per-lane
+  // pointer stays live across the loop)
+  const u32x4* wc = (const u32x4*)Wc;  // tile nt, group gr, part p at ((nt * G + gr) * 2 + p) * 64 + lane
+  const u32x4* ws = (const u32x4*)Ws;  // tile nt, group gr at (nt * G + gr) * 4 + 2 * h
+  const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
   for (int gi = wave; gi < ngr; gi += WAVES) {
     const int gr = g0 + gi;
@@ -789,8 +791,8 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
       const int64_t tg = (int64_t)(nt0 + t) * G + gr;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        cw[t][p] = load_weight<MT>(wc + (tg * 2 + p) * 64);
-        sw[t][p] = ws[tg * 4 + p];
+        cw[t][p] = load_weight<MT>(wc + (tg * 2 + p) * 64 + lane);
+        sw[t][p] = ws[tg * 4 + p + 2 * h];
       }
     }
     f32x16 acc[MT][TP];
@@ -805,8 +807,8 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
       for (int i = 0; i < MT; ++i)
         if (MT == 1 || i < mcount) {
           const int64_t o = ((int64_t)i * g.KB + gr * GB + b) * 64;
-          xh[i] = xp[o];
-          xl[i] = xq[o];
+          xh[i] = xp[o + lane];
+          xl[i] = xq[o + lane];
         }
 #pragma unroll
       for (int t = 0; t < TP; ++t) {
