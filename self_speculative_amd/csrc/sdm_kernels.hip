@@ -504,6 +504,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   // launch, whose missing tiles load tile nt0 again and are not finished
   const int tvalid = MT == 4 ? min(TP, g.NT - nt0) : TP;
   auto tl = [&](int t) { return MT == 4 && t >= tvalid ? 0 : t; };
+  // launches of one or two activation tiles hold exactly that many rows'
+  // tiles (the launcher picks MT from the tile count); four-tile launches
+  // skip the tiles past the rows
+  auto use = [&](int i) { return MT <= 2 || i < mcount; };
   const u32x4* wp = (const u32x4*)W + (int64_t)nt0 * g.KB * 64 + lane;  // tile nt0 + t at t * KB * 64
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
       for (int u = 0; u < U; ++u) wv[t][u] = load_weight<MT>(wp + ((int64_t)tl(t) * g.KB + kb + boff(u)) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (i < mcount) {
+      if (use(i)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t o = ((int64_t)i * g.KB + kb + boff(u)) * 64;
@@ -525,13 +529,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
           xl[i][u] = xq[o];
         }
       }
+    // a few-row launch requests its whole batch before the first product
+    // (the compiler would otherwise trade loads in flight for registers)
+    if constexpr (MT <= 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int t = 0; t < TP; ++t)
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-          if (i < mcount) {
+          if (use(i)) {
             acc[i][t] = mfma32(wv[t][u], xh[i][u], acc[i][t]);
             acc[i][t] = mfma32(wv[t][u], xl[i][u], acc[i][t]);
           }
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
     for (int t = 0; t < TP; ++t) wv[t] = load_weight<MT>(wp + ((int64_t)tl(t) * g.KB + kb) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (i < mcount) {
+      if (use(i)) {
         const int64_t o = ((int64_t)i * g.KB + kb) * 64;
         const u32x4 xh = xp[o], xl = xq[o];
 #pragma unroll
@@ -805,7 +812,7 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
       u32x4 xh[MT], xl[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i)
-        if (MT == 1 || i < mcount) {
+        if (MT <= 2 || i < mcount) {
           const int64_t o = ((int64_t)i * g.KB + gr * GB + b) * 64;
           xh[i] = xp[o + lane];
           xl[i] = xq[o + lane];
@@ -815,7 +822,7 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
         const u32x4 a = w4_operand(cw[t][b >> 2][b & 3]);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-          if (MT == 1 || i < mcount) {
+          if (MT <= 2 || i < mcount) {
             acc[i][t] = mfma32(a, xh[i], acc[i][t]);
             acc[i][t] = mfma32(a, xl[i], acc[i][t]);
           }
