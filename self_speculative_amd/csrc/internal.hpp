@@ -134,6 +134,7 @@ struct GemmShape {
   int S;                 // workgroups splitting K (EPI_PARTIAL only)
   int WAVES;             // waves per workgroup, splitting the workgroup's K range
   int TP;                // weight tiles per workgroup
+  int ROWS;              // activation rows (a one-tile launch loads only these)
 };
 
 constexpr int kGemmTargetGroups = 256;  // one workgroup per compute unit
@@ -155,6 +156,7 @@ inline GemmShape gemm_config(int epi, int N, int K, int rows) {
   g.NT = N / 32;
   g.KB = K / 16;
   g.MTILES = (rows + 31) / 32;
+  g.ROWS = rows;
   g.S = 1;
   if (epi == EPI_PARTIAL) {
     // enough splits for two workgroups per compute unit (two waves per SIMD,
@@ -230,6 +232,7 @@ inline GemmShape gemm_config_w4(int epi, int N, int K, int rows) {
   g.NT = N / 32;
   g.KB = K / 16;
   g.MTILES = (rows + 31) / 32;
+  g.ROWS = rows;
   g.S = 1;
   if (epi == EPI_PARTIAL) {
     auto ok = [&](int s) {

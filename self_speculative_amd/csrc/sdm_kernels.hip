@@ -451,7 +451,7 @@ __device__ __forceinline__ u32x4 load_weight(const u32x4* p) {
   else return *p;
 }
 
-template <int EPI, int MT, int TP, int U, int WAVES>
+template <int EPI, int MT, int TP, int U, int WAVES, bool XMASK = false>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X, int64_t x_plane,
                                                           GemmShape g, EpiArgs ea) {
@@ -511,17 +511,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
   const u32x4* wp = (const u32x4*)W + (int64_t)nt0 * g.KB * 64 + lane;  // tile nt0 + t at t * KB * 64
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64 + lane;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
+  // XMASK (a one-tile launch of fewer than 32 rows, such as a one-row AR
+  // step): only the lanes of the launch's rows load activations; the other
+  // operand columns stay zero, and an MFMA output column depends on its own
+  // operand column alone, so the rows' results are the same bits.
+  static_assert(!XMASK || MT == 1, "row masking serves one-tile launches");
+  const bool xrow = !XMASK || (lane & 31) < g.ROWS;
   int kb = kbase + wave * kGemmChunk;  // first block of this wave's next chunk
+  u32x4 xh[MT][U], xl[MT][U];
+  if constexpr (XMASK) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) xh[0][u] = xl[0][u] = u32x4{0u, 0u, 0u, 0u};
+  }
   for (; kb + (CB - 1) * kstep + kGemmChunk <= kfull; kb += CB * kstep) {
     u32x4 wv[TP][U];
-    u32x4 xh[MT][U], xl[MT][U];
 #pragma unroll
     for (int t = 0; t < TP; ++t)
 #pragma unroll
       for (int u = 0; u < U; ++u) wv[t][u] = load_weight<MT>(wp + ((int64_t)tl(t) * g.KB + kb + boff(u)) * 64);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (use(i)) {
+      if (use(i) && xrow) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t o = ((int64_t)i * g.KB + kb + boff(u)) * 64;
@@ -551,7 +561,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_bf16(const uint16_t* __rest
     for (int i = 0; i < MT; ++i)
       if (use(i)) {
         const int64_t o = ((int64_t)i * g.KB + kb) * 64;
-        const u32x4 xh = xp[o], xl = xq[o];
+        u32x4 xh = u32x4{0u, 0u, 0u, 0u}, xl = u32x4{0u, 0u, 0u, 0u};
+        if (xrow) {
+          xh = xp[o];
+          xl = xq[o];
+        }
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
           acc[i][t] = mfma32(wv[t], xh, acc[i][t]);
@@ -641,7 +655,13 @@ static void launch_gemm_w(const uint16_t* W, const uint16_t* X, int64_t x_plane,
              blk(64 * WAVES);
   // weight loads in flight per wave: 16 tiles at TP 1, 4 * TP otherwise
   constexpr int U1 = WAVES == 8 ? 8 : 16;
-  if (MT == 1) {
+  if (MT == 1 && g.ROWS < 32) {
+    // fewer rows than the tile: only those rows' activation lanes load
+    if (TP == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 1, U1, WAVES, true>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 2, 4, WAVES, true>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else if (TP == 3) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 3, 4, WAVES, true>), grd, blk, 0, st, W, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_bf16<EPI, 1, 4, 4, WAVES, true>), grd, blk, 0, st, W, X, x_plane, g, ea);
+  } else if (MT == 1) {
     if (TP == 1) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 1, U1, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
     else if (TP == 2) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 2, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
     else if (TP == 3) SDM_LAUNCH((k_gemm_bf16<EPI, 1, 3, 4, WAVES>), grd, blk, 0, st, W, X, x_plane, g, ea);
@@ -757,7 +777,7 @@ __device__ __forceinline__ float w4_scale(const u32x4 (&s)[2], int r) {
 // workgroup's K range goes to the waves by scale group, round robin; a wave
 // adds its groups in increasing order and the waves' totals meet in LDS in
 // wave order, so a row's result does not depend on the batch it is in.
-template <int EPI, int MT, int TP>
+template <int EPI, int MT, int TP, bool XMASK = false>
 __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __restrict__ Wc,
                                                            const uint16_t* __restrict__ Ws,
                                                            const uint16_t* __restrict__ X, int64_t x_plane,
@@ -790,6 +810,11 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
   const u32x4* ws = (const u32x4*)Ws;  // tile nt, group gr at (nt * G + gr) * 4 + 2 * h
   const u32x4* xp = (const u32x4*)X + (int64_t)mt0 * g.KB * 64;
   const u32x4* xq = xp + (x_plane >> 3);  // lo plane
+  // XMASK (a one-tile launch of fewer than 32 rows): only its rows' lanes
+  // load activations; the other operand columns stay zero, and the rows'
+  // results are the same bits
+  static_assert(!XMASK || MT == 1, "row masking serves one-tile launches");
+  const bool xrow = !XMASK || (lane & 31) < g.ROWS;
   for (int gi = wave; gi < ngr; gi += WAVES) {
     const int gr = g0 + gi;
     u32x4 cw[TP][2], sw[TP][2];
@@ -810,9 +835,10 @@ __global__ __launch_bounds__(64 * kW4Waves) void k_gemm_w4(const uint8_t* __rest
 #pragma unroll
     for (int b = 0; b < GB; ++b) {
       u32x4 xh[MT], xl[MT];
+      if constexpr (XMASK) xh[0] = xl[0] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < MT; ++i)
-        if (MT <= 2 || i < mcount) {
+        if ((MT <= 2 || i < mcount) && xrow) {
           const int64_t o = ((int64_t)i * g.KB + gr * GB + b) * 64;
           xh[i] = xp[o + lane];
           xl[i] = xq[o + lane];
@@ -887,7 +913,13 @@ static hipError_t launch_gemm_w4_epi(const uint8_t* W, const uint16_t* X, int64_
   if (g.WAVES != kW4Waves || MT * TP > 4 || g.NT % TP || g.KB % (g.S * kW4GroupBlocks)) return hipErrorInvalidValue;
   const uint16_t* Ws = (const uint16_t*)(W + w4_scale_offset((int64_t)g.NT * 32, (int64_t)g.KB * 16));
   const dim3 grd(g.NT / TP, g.S, (g.MTILES + MT - 1) / MT), blk(64 * kW4Waves);
-  if (MT == 1) {
+  if (MT == 1 && g.ROWS < 32) {
+    // fewer rows than the tile: only those rows' activation lanes load
+    if (TP == 1) SDM_LAUNCH((k_gemm_w4<EPI, 1, 1, true>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else if (TP == 2) SDM_LAUNCH((k_gemm_w4<EPI, 1, 2, true>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else if (TP == 3) SDM_LAUNCH((k_gemm_w4<EPI, 1, 3, true>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+    else SDM_LAUNCH((k_gemm_w4<EPI, 1, 4, true>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
+  } else if (MT == 1) {
     if (TP == 1) SDM_LAUNCH((k_gemm_w4<EPI, 1, 1>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
     else if (TP == 2) SDM_LAUNCH((k_gemm_w4<EPI, 1, 2>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);
     else if (TP == 3) SDM_LAUNCH((k_gemm_w4<EPI, 1, 3>), grd, blk, 0, st, W, Ws, X, x_plane, g, ea);

@@ -219,6 +219,35 @@ def test_bf16_selfspec_equals_ar_on_gpu(gm):
     assert ss.tokens == ar.tokens
 
 
+def test_bf16_short_blocks_bit_identical(gm):
+    """Launches of fewer than 32 rows load only their rows' activation lanes:
+    causal blocks of 1, 7 and 31 tokens and the one-row AR step give each row
+    the bits of the same row in a full 32-row block."""
+    p = W.prompt_ids(SHAPE, 45, seed=26)
+    toks = W.prompt_ids(SHAPE, B, seed=27)
+    gm.seq_reset(5)
+    nxt = torch.empty(1, dtype=torch.int32, device=DEV)
+    gm.prefill(5, _i32(p), nxt)
+    full = torch.empty((B, SHAPE.vocab), dtype=torch.float32, device=DEV)
+    a = torch.empty(B, dtype=torch.int32, device=DEV)
+    acc = torch.empty(1, dtype=torch.int32, device=DEV)
+    print("bf16 full 32-row causal block", flush=True)
+    gm.verify_block([5], _i32(toks), B, a, acc, full)
+    torch.cuda.synchronize()
+    ref = full.cpu().numpy()
+    for b in (1, 7, 31):
+        print(f"bf16 causal block of {b} rows", flush=True)
+        lg = torch.empty((b, SHAPE.vocab), dtype=torch.float32, device=DEV)
+        gm.verify_block([5], _i32(toks[:b]), b, a[:b], acc, lg)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(lg.cpu().numpy(), ref[:b])
+    print("bf16 one-row AR step", flush=True)
+    lg = torch.empty((1, SHAPE.vocab), dtype=torch.float32, device=DEV)
+    gm.decode_ar(5, _i32([toks[0]]), nxt, lg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lg.cpu().numpy(), ref[:1])
+
+
 def test_bf16_perfect_draft_and_planted_mismatch(gm):
     from self_speculative_amd import decode as D
     p = W.prompt_ids(SHAPE, 40, seed=25)
