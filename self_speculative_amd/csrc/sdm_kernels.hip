@@ -1879,14 +1879,42 @@ __device__ __forceinline__ SamplePart part_empty() {
   return p;
 }
 
-// The workgroup's partial merged by thread 0 in thread order (deterministic).
+// part_merge is commutative bit for bit (the weighted sum's two products
+// add in either order to the same value; the maxima and the lower-id tie
+// rule are symmetric), so a wave's parts merge in a fixed butterfly over
+// lane distances 32, 16, ..., 1: a deterministic tree of six levels instead
+// of a chain of 63 dependent merges.  Lane 0's result is the one used.
+__device__ __forceinline__ SamplePart part_shfl_xor(const SamplePart& a, int o) {
+  SamplePart b;
+  b.best = __shfl_xor(a.best, o);
+  b.second = __shfl_xor(a.second, o);
+  b.m = __shfl_xor(a.m, o);
+  b.s = __shfl_xor(a.s, o);
+  b.idx = __shfl_xor(a.idx, o);
+  b.pad0 = b.pad1 = b.pad2 = 0;
+  return b;
+}
+__device__ __forceinline__ SamplePart part_wave_merge(SamplePart a) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const SamplePart b = part_shfl_xor(a, o);
+    part_merge(a, b);
+  }
+  return a;
+}
+
+// The workgroup's partial: each wave's 64 parts by the butterfly, then the
+// four wave results by thread 0 in wave order (deterministic).
 __device__ void part_reduce_store(SamplePart mine, SamplePart* out) {
-  __shared__ SamplePart sp[256];
-  sp[threadIdx.x] = mine;
+  static_assert(sizeof(SamplePart) == 32, "a part is two 16-byte words");
+  __shared__ SamplePart sp[4];
+  const SamplePart w = part_wave_merge(mine);
+  if ((threadIdx.x & 63) == 0) sp[threadIdx.x >> 6] = w;
   __syncthreads();
   if (threadIdx.x == 0) {
     SamplePart a = sp[0];
-    for (int t = 1; t < 256; ++t) part_merge(a, sp[t]);
+#pragma unroll
+    for (int t = 1; t < 4; ++t) part_merge(a, sp[t]);
     *out = a;
   }
 }
@@ -1924,15 +1952,16 @@ __global__ __launch_bounds__(256) void k_sample_partial(FinishArgs f, int r0, in
   part_reduce_store(a, f.parts + (int64_t)r * kSampleParts + blockIdx.x);
 }
 
-// Merge a row's parts (part order): tok, gap, lse, ln p(tok) and, with a
-// probe, ln p(probe).  One thread per row of the launch.
-__global__ void k_sample_merge(FinishArgs f, int r0, int nrows, const int* probe) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// Merge a row's parts: tok, gap, lse, ln p(tok) and, with a probe,
+// ln p(probe).  One wave per row of the launch; lane q loads part q and the
+// butterfly merges them.
+static_assert(kSampleParts == 64, "one part per lane of a merging wave");
+__global__ __launch_bounds__(64) void k_sample_merge(FinishArgs f, int r0, int nrows, const int* probe) {
+  const int i = blockIdx.x;
   if (i >= nrows) return;
   const int r = r0 + i;
-  const SamplePart* pp = f.parts + (int64_t)r * kSampleParts;
-  SamplePart a = pp[0];
-  for (int q = 1; q < kSampleParts; ++q) part_merge(a, pp[q]);
+  const SamplePart a = part_wave_merge(f.parts[(int64_t)r * kSampleParts + threadIdx.x]);
+  if (threadIdx.x != 0) return;
   const float lse = a.m + logf(a.s);
   const float* row = f.logits + (int64_t)r * f.V;
   f.tok[r] = a.idx;
@@ -1986,11 +2015,12 @@ __global__ __launch_bounds__(256) void k_residual_partial(FinishArgs f) {
   part_reduce_store(a, f.parts + blockIdx.x);
 }
 
-__global__ void k_residual_merge(FinishArgs f) {
+// One wave: lane q loads part q, the butterfly merges them.
+__global__ __launch_bounds__(64) void k_residual_merge(FinishArgs f) {
   const int k = f.accept[0] - 1;
-  if (threadIdx.x != 0 || k >= f.T - 1) return;
-  SamplePart a = f.parts[0];
-  for (int q = 1; q < kSampleParts; ++q) part_merge(a, f.parts[q]);
+  if (k >= f.T - 1) return;
+  const SamplePart a = part_wave_merge(f.parts[threadIdx.x]);
+  if (threadIdx.x != 0) return;
   // no id with p > q left after rounding: the verify row's own sample at that position
   f.next[0] = a.idx == 0x7fffffff ? f.tok[k] : a.idx;
 }
@@ -2022,12 +2052,12 @@ static hipError_t launch_finish_sample(const FinishArgs& f, hipStream_t st) {
   } else if (f.mode == FIN_SAMPLE_DRAFT) {
     // bidirectional rows 1..T-1 predict their own positions n + t
     SDM_LAUNCH(k_sample_partial, dim3(kSampleParts, f.T - 1), dim3(256), 0, st, f, 1, n + 1, (int)PURPOSE_DRAFT);
-    SDM_LAUNCH(k_sample_merge, dim3((f.T + 62) / 64), dim3(64), 0, st, f, 1, f.T - 1, (const int*)nullptr);
+    SDM_LAUNCH(k_sample_merge, dim3(f.T - 1), dim3(64), 0, st, f, 1, f.T - 1, (const int*)nullptr);
     SDM_LAUNCH(k_finish_sample_draft, dim3((f.T + 63) / 64), dim3(64), 0, st, f);
   } else {
     // causal rows 0..T-1 predict n + t + 1; row t probes draft token block[t + 1]
     SDM_LAUNCH(k_sample_partial, dim3(kSampleParts, f.T), dim3(256), 0, st, f, 0, n + 1, (int)PURPOSE_SAMPLE);
-    SDM_LAUNCH(k_sample_merge, dim3((f.T + 62) / 64), dim3(64), 0, st, f, 0, f.T - 1, (const int*)(f.block + 1));
+    SDM_LAUNCH(k_sample_merge, dim3(f.T - 1), dim3(64), 0, st, f, 0, f.T - 1, (const int*)(f.block + 1));
     SDM_LAUNCH(k_sample_merge, dim3(1), dim3(64), 0, st, f, f.T - 1, 1, (const int*)nullptr);
     SDM_LAUNCH(k_finish_sample_verify, dim3(1), dim3(64), 0, st, f);
     SDM_LAUNCH(k_residual_partial, dim3(kSampleParts), dim3(256), 0, st, f);
