@@ -1761,38 +1761,75 @@ __global__ __launch_bounds__(256) void k_select_rows(const float4* __restrict__ 
   }
 }
 
-// The mode rules on a sequence's rows.  One workgroup (one thread) per slot.
-__global__ void k_finish_mode(FinishArgs f) {
-  const int slot = blockIdx.x;
-  if (threadIdx.x != 0) return;
+// Wave sums and the (confidence, lowest index) maximum for k_finish_mode.
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ void wave_best(float& c, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float c2 = __shfl_xor(c, o);
+    const int i2 = __shfl_xor(i, o);
+    if (c2 > c || (c2 == c && i2 < i)) {
+      c = c2;
+      i = i2;
+    }
+  }
+}
+
+// The mode rules on a sequence's rows.  One wave per slot; lane j takes
+// positions j, j + 64, ... so that a block's loads are issued together.
+__global__ __launch_bounds__(64) void k_finish_mode(FinishArgs f) {
+  const int slot = blockIdx.x, lane = threadIdx.x;
   const int T = f.T;
   const int r0 = slot * T;
   if (f.mode == FIN_NEXT) {
-    if (slot == 0) f.next[0] = f.tok[r0 + T - 1];
+    if (slot == 0 && lane == 0) f.next[0] = f.tok[r0 + T - 1];
   } else if (f.mode == FIN_DRAFT) {
-    f.block[r0] = f.anchor[slot];
-    for (int j = 1; j < T; ++j) f.block[r0 + j] = f.tok[r0 + j];
+    for (int j = lane; j < T; j += 64) f.block[r0 + j] = j == 0 ? f.anchor[slot] : f.tok[r0 + j];
   } else if (f.mode == FIN_VERIFY || (f.mode == FIN_QUAD && slot == 0)) {
-    int k = 0;
-    while (k + 1 <= T - 1 && f.block[r0 + k + 1] == f.tok[r0 + k]) ++k;
-    for (int j = 0; j < T; ++j) f.ar_out[r0 + j] = f.tok[r0 + j];
-    f.accept[slot] = k + 1;
+    // k: the leading drafts that equal the AR argmax of the row before them;
+    // the first mismatch by a ballot (wave-uniform), every load of a chunk
+    // in flight together
+    int k = T - 1;
+    for (int j0 = 0; j0 < T - 1; j0 += 64) {
+      const int j = j0 + lane;
+      const bool miss = j < T - 1 && f.block[r0 + j + 1] != f.tok[r0 + j];
+      const unsigned long long b = __ballot(miss);
+      if (b) {
+        k = j0 + __ffsll(b) - 1;
+        break;
+      }
+    }
+    for (int j = lane; j < T; j += 64) f.ar_out[r0 + j] = f.tok[r0 + j];
+    if (lane == 0) f.accept[slot] = k + 1;
   } else if (f.mode == FIN_QUAD) {
     // candidate k = slot - 1: the next block should the accept length be k + 1
     const int k = slot - 1;
-    f.next_blocks[k * T] = f.tok[k];
-    for (int j = 1; j < T; ++j) f.next_blocks[k * T + j] = f.tok[r0 + j];
+    for (int j = lane; j < T; j += 64) f.next_blocks[k * T + j] = j == 0 ? f.tok[k] : f.tok[r0 + j];
   } else {  // FIN_DIFFUSE
     // masked positions: the unmask rule; written positions: the revise rule
     // (tau_revise >= 1 never fires, conf <= 1).  Each decision reads only its
-    // own position's token before the step, and `best` is fixed first.
-    int best = -1, n_m = 0, n_u = 0, n_r = 0;
-    for (int i = 0; i < T; ++i)
+    // own position's token before the step, and `best` (the most confident
+    // masked position, the lowest on ties) is fixed first.
+    float bc = -INFINITY;
+    int bi = 0x7fffffff, n_m = 0;
+    for (int i = lane; i < T; i += 64)
       if (f.block[r0 + i] == f.mask_id) {
         ++n_m;
-        if (best < 0 || f.conf[r0 + i] > f.conf[r0 + best]) best = i;
+        const float c = f.conf[r0 + i];
+        if (bi == 0x7fffffff || c > bc) {  // ascending i in a lane: strict > keeps the lowest
+          bc = c;
+          bi = i;
+        }
       }
-    for (int i = 0; i < T; ++i) {
+    wave_best(bc, bi);
+    n_m = wave_sum_int(n_m);
+    const int best = bi == 0x7fffffff ? -1 : bi;
+    int n_u = 0, n_r = 0;
+    for (int i = lane; i < T; i += 64) {
       if (f.conf_out) f.conf_out[r0 + i] = f.conf[r0 + i];
       const int cur = f.block[r0 + i], t = f.tok[r0 + i];
       if (cur != f.mask_id) {
@@ -1805,8 +1842,12 @@ __global__ void k_finish_mode(FinishArgs f) {
         ++n_u;
       }
     }
-    f.n_masked[slot] = n_m - n_u;
-    if (f.n_revised) f.n_revised[slot] = n_r;
+    n_u = wave_sum_int(n_u);
+    n_r = wave_sum_int(n_r);
+    if (lane == 0) {
+      f.n_masked[slot] = n_m - n_u;
+      if (f.n_revised) f.n_revised[slot] = n_r;
+    }
   }
 }
 
